@@ -1,0 +1,273 @@
+"""Benchmark of the micro-scaled FP4 hot path on one MI355X.
+
+Default workload (one step = the whole path on one batch):
+  Hadamard-32 + MXFP4 quantization of bf16 activations A [8192, 8192] (fp4_quantize), then
+  the W4A4 MXFP4 GEMM C = A W^T against offline-rotated MXFP4 weights W [28672, 8192]
+  (fp4_gemm, bf16 out).  Inputs are seeded synthetic stand-ins (N(0,1) activations,
+  N(0, 0.02) weights) already resident in HBM when timing starts.
+
+Prints one JSON line: whole-step throughput in TFLOP/s (2 M N K per step), the roofline
+of the dominant kernel (the GEMM, against the 10.1 PFLOP/s dense FP4 MFMA peak) and of the
+quantization kernel (against 8 TB/s HBM), both from HIP events recorded around each launch
+inside the timed loop, and the CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload) time one kernel each against the HBM roofline, rotating
+through >= 1 GiB of buffer sets so the 256 MB Infinity Cache cannot serve them.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import microscaled_fp4_quantization_block_amd as fp4  # noqa: E402
+from microscaled_fp4_quantization_block_amd import workloads as W  # noqa: E402
+
+METRIC = "FP4 quantize GB/s (% HBM peak) + W4A4 MXFP4 GEMM TFLOPS (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+FP4_PEAK_TFLOPS = 10100.0
+DEV = "cuda:0"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if one exists."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            return json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events around launches on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline_gemm(a_bf16, w_bf16, rows=64, cols=2048):
+    """Oracle (float64 numpy) on a bounded sample of the step: Hadamard-32 MXFP4 of `rows`
+    activation rows, then their GEMM against `cols` weight rows quantized the same way
+    (untimed setup).  Throughput in the step's unit: 2 rows cols K / time."""
+    from threadpoolctl import threadpool_info
+    from oracle import gemm, mxfp4
+    K = a_bf16.shape[1]
+    a = W.values(a_bf16[:rows])
+    w = W.values(w_bf16[:cols])
+    qw = mxfp4.quantize(w, hadamard=32)                       # offline weights (untimed)
+    t0 = time.perf_counter()
+    qa = mxfp4.quantize(a, hadamard=32)
+    c = gemm.tile(qa["packed"], qa["scales"], qw["packed"], qw["scales"], np.arange(rows), np.arange(cols))
+    dt = time.perf_counter() - t0
+    assert c.shape == (rows, cols)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": 2.0 * rows * cols * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"Hadamard-32 MXFP4 quantization of {rows} activation rows + float64 GEMM against "
+                      f"{cols} oracle-quantized weight rows, K={K} ({rows}x{cols} of the "
+                      f"{a_bf16.shape[0]}x{w_bf16.shape[0]} output)"}
+
+
+def cpu_baseline_bytes(fn, nbytes, what):
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "seconds": dt,
+            "sample": what}
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def run_w4a4_gemm(args):
+    wl = W.WORKLOADS["w4a4_gemm"]
+    M, K = wl.shape
+    N = wl.extra["N"]
+    a_cpu = W.gemm_activations((M, K), wl.seed)
+    w_cpu = W.gemm_weights(N, K, wl.extra["weight_seed"], wl.extra["weight_std"])
+    a = a_cpu.to(DEV)
+    w = w_cpu.to(DEV)
+    # offline: rotate + quantize the weights (not part of the step)
+    b_codes, b_scales, _ = fp4.fp4_quantize(w, "mxfp4", 32)
+    del w
+    a_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    a_scales = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+
+    def step(tq=None, tg=None):
+        s = tq.start() if tq else None
+        fp4.fp4_quantize(a, "mxfp4", 32, codes=a_codes, scales=a_scales)
+        if tq:
+            tq.stop(s)
+            s = tg.start()
+        fp4.fp4_gemm(a_codes, a_scales, b_codes, b_scales, c=c)
+        if tg:
+            tg.stop(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tq, tg = Timer(), Timer()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tq, tg)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    gemm_ms, quant_ms = tg.mean_ms(), tq.mean_ms()
+    quant_bytes = M * K * 2 + M * K // 2 + M * K // 32          # bf16 in, codes + E8M0 out
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1/e8m0 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no model weights or datasets)",
+        "config": {"workload": "w4a4_gemm: Hadamard-32 MXFP4 quantization of A bf16 8192x8192 + "
+                               "W4A4 MXFP4 GEMM against rotated MXFP4 weights 28672x8192, bf16 out",
+                   "M": M, "N": N, "K": K, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / FP4_PEAK_TFLOPS, "traffic": _traffic("gemm_w4a4"),
+                     "kernel": "k_gemm", "kernel_ms": gemm_ms, "flop_per_launch": flops},
+        "roofline_quantize": {"bound": "hbm", "achieved": quant_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": quant_gbs / HBM_PEAK_GBS, "traffic": _traffic("quant_mx_h32_a"),
+                              "kernel": "k_quant_mx<bf16,32>", "kernel_ms": quant_ms,
+                              "bytes_per_launch": quant_bytes},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_gemm(a_cpu, w_cpu)
+    return out
+
+
+def _rotating(make, nbytes_per_set, min_total=1 << 30):
+    sets = max(2, -(-min_total // max(nbytes_per_set, 1)))
+    return [make() for _ in range(sets)]
+
+
+def run_memory_workload(args):
+    name = args.workload
+    wl = W.WORKLOADS[name]
+    if name == "mxfp4_h32":
+        x_cpu = W.mxfp4_h32_input(wl.shape, wl.seed)
+        M, K = wl.shape
+        nbytes = M * K * 2 + M * K // 2 + M * K // 32
+
+        def make():
+            return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
+                    torch.empty((M, K // 32), dtype=torch.uint8, device=DEV))
+
+        def launch(s):
+            fp4.fp4_quantize(s[0], "mxfp4", 32, codes=s[1], scales=s[2])
+        kernel = "k_quant_mx<bf16,32>"
+    elif name == "dualscale_pack":
+        x_cpu = W.student_t_input(wl.shape, wl.seed)
+        M, K = wl.shape
+        nbytes = M * K * 2 + M * K // 2 + M * K // 16 + 4 * M * K // 128
+
+        def make():
+            return (x_cpu.to(DEV), torch.empty(fp4.fp4_pack_bytes(M, K), dtype=torch.uint8, device=DEV))
+
+        def launch(s):
+            fp4.fp4_pack(s[0], packed=s[1])
+        kernel = "k_pack"
+    elif name == "arcquant":
+        x_cpu = W.arcquant_input(wl.shape, wl.seed)
+        M, K = wl.shape
+        S = wl.extra["S"]
+        perm = torch.from_numpy(W.calibration_order(x_cpu)).to(DEV)
+        ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+        fp4.fp4_residual_quantize(x_cpu.to(DEV), perm, S, tensor_scale=ts)        # calibrate once
+        nbytes = M * K * 2 + K * 4 + M * (K + S) // 2 + M * (K + S) // 16 + 4
+
+        def make():
+            return (x_cpu.to(DEV), torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=DEV),
+                    torch.empty((M, (K + S) // 16), dtype=torch.uint8, device=DEV))
+
+        def launch(s):
+            fp4.fp4_residual_quantize(s[0], perm, S, codes=s[1], scales=s[2], tensor_scale=ts, mode="given")
+        kernel = "k_arcquant<false> (static tensor scale)"
+    elif name == "nvfp4_roundtrip":
+        x_cpu = W.nvfp4_roundtrip_input(wl.shape, wl.seed)
+        M, K = wl.shape
+        nbytes = M * K * 4 + M * K // 2 + M * K // 16 + 4
+
+        def make():
+            return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
+                    torch.empty((M, K // 16), dtype=torch.uint8, device=DEV),
+                    torch.zeros(1, dtype=torch.float32, device=DEV))
+
+        def launch(s):
+            fp4.fp4_quantize(s[0], "nvfp4", 0, codes=s[1], scales=s[2], tensor_scale=s[3])
+        kernel = "NVFP4 exact quantize (amax pass + quant)"
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    sets = _rotating(make, nbytes)
+    for i in range(args.warmup):
+        launch(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t = Timer()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = t.start()
+        launch(sets[i % len(sets)])
+        t.stop(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = t.mean_ms()
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    out = {"metric": METRIC, "value": nbytes / (wall / args.steps) / 1e9, "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp4 out",
+           "data": "synthetic", "config": {"workload": f"{name}: {wl.description}"},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(name), "kernel": kernel,
+                        "kernel_ms": kms, "bytes_per_launch": nbytes, "buffer_sets": len(sets)}}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="w4a4_gemm", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+                                   "not implemented (run with --gpus 1)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    fp4.lib()                                   # fail loudly if the HIP library is missing
+    out = run_w4a4_gemm(args) if args.workload == "w4a4_gemm" else run_memory_workload(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,290 @@
+// Device-side building blocks shared by the gfx950 kernels: bf16 widening, in-register
+// fast Walsh-Hadamard transforms, E2M1 / E4M3 / E8M0 encoding and wave reductions.
+//
+// Format definitions follow OCP MX v1.0 (E2M1 elements, E8M0 scales) and OCP FP8 (E4M3
+// scales); the pages name the formats (ARCQuant summary, gist.science: NVFP4 blocks of 16
+// with E2M1 elements; MR-GPTQ abstract, hyper.ai: power-of-two MXFP4 scales) but give no
+// bit layouts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+// --------------------------------------------------------------------------- bf16 / fp32
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Nearest-even fp32 -> bf16 for finite values.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+}
+
+// Load N consecutive elements (N % 8 == 0) as fp32 with 16-byte loads.
+template <int N>
+__device__ __forceinline__ void load_bf16(const uint16_t* p, float* v) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    uint4 w = q[i];
+    v[8 * i + 0] = bf16_lo(w.x); v[8 * i + 1] = bf16_hi(w.x);
+    v[8 * i + 2] = bf16_lo(w.y); v[8 * i + 3] = bf16_hi(w.y);
+    v[8 * i + 4] = bf16_lo(w.z); v[8 * i + 5] = bf16_hi(w.z);
+    v[8 * i + 6] = bf16_lo(w.w); v[8 * i + 7] = bf16_hi(w.w);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void load_f32(const float* p, float* v) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    float4 w = q[i];
+    v[4 * i + 0] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_f32(float* p, const float* v) {
+  float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+template <int N>
+__device__ __forceinline__ void store_bf16(uint16_t* p, const float* v) {
+  uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    uint4 w;
+    w.x = pack_bf16x2(v[8 * i + 0], v[8 * i + 1]);
+    w.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
+    w.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
+    w.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
+    q[i] = w;
+  }
+}
+
+// --------------------------------------------------------------------------- Hadamard
+
+// Unnormalised Sylvester-ordered Walsh-Hadamard transform of v[0..N) in registers:
+// log2(N) butterfly stages of N/2 add/sub pairs.  Result = (sqrt(N) H_N) v.
+template <int N>
+__device__ __forceinline__ void fwht_inplace(float* v) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// 1/sqrt(n) rounded to fp32 (n = 16 is exact).
+template <int N> struct InvSqrt;
+template <> struct InvSqrt<16> { static constexpr float v = 0.25f; };
+template <> struct InvSqrt<32> { static constexpr float v = 0.17677669529663688f; };
+template <> struct InvSqrt<128> { static constexpr float v = 0.08838834764831845f; };
+
+// Orthonormal H_B on every contiguous B-block of v[0..N).
+template <int N, int B>
+__device__ __forceinline__ void block_hadamard(float* v) {
+  if constexpr (B > 1) {
+#pragma unroll
+    for (int b = 0; b < N; b += B) fwht_inplace<B>(v + b);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] *= InvSqrt<B>::v;
+  }
+}
+
+// Two-level FWHT of one 128-group held in registers (index 16 g + j): H_16 inside each
+// micro-group g, then H_8 across the micro-groups at each position j, normalised once.
+__device__ __forceinline__ void two_level_fwht128(float* v) {
+#pragma unroll
+  for (int g = 0; g < 8; ++g) fwht_inplace<16>(v + 16 * g);     // level 1
+#pragma unroll
+  for (int h = 16; h < 128; h <<= 1) {                            // level 2: strides 16, 32, 64
+#pragma unroll
+    for (int i = 0; i < 128; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 128; ++i) v[i] *= InvSqrt<128>::v;
+}
+
+// --------------------------------------------------------------------------- E2M1
+
+// Round-to-nearest-even E2M1 codes of v[i] / scale for 32 values, scale a power of two
+// (gfx950 v_cvt_scalef32_pk_fp4_f32; only the exponent of `scale` is used, and the
+// result is the exact RNE decision of the quotient, saturating at +-6, sign kept on 0).
+__device__ __forceinline__ uint4 e2m1_encode32(const float* v, float scale) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 0], v[8 * i + 1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 2], v[8 * i + 3], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 4], v[8 * i + 5], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 6], v[8 * i + 7], scale, 3);
+    w[i] = r;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint2 e2m1_encode16(const float* v, float scale) {
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 0], v[8 * i + 1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 2], v[8 * i + 3], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 4], v[8 * i + 5], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * i + 6], v[8 * i + 7], scale, 3);
+    w[i] = r;
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// Decode the 8 codes of one packed word: V(code) * scale for a power-of-two scale.
+__device__ __forceinline__ void e2m1_decode8(uint32_t w, float scale, float* v) {
+  auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+  auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+  auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+  auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+  v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+  v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
+}
+
+// Binary32 value whose RNE rounding to E2M1 equals the RNE rounding of the float64 q:
+// q is clamped to [2^-10, 6] (which changes no E2M1 decision), truncated to binary32 and
+// its last bit set when the truncation was inexact ("round to odd").  Rounding to odd
+// into a format with at least two more bits than the target keeps the final
+// round-to-nearest-even exact (Boldo & Melquiond, "Emulation of FMA and correctly
+// rounded sums: proved algorithms using rounding to odd", IEEE TC 2008).
+__device__ __forceinline__ float round_to_odd_f32(double q) {
+  q = fmin(fmax(q, 0x1p-10), 6.0);
+  uint64_t b = (uint64_t)__double_as_longlong(q);
+  uint32_t hi = (uint32_t)(b >> 32) - (896u << 20);    // rebias exponent 1023 -> 127
+  uint32_t lo = (uint32_t)b;
+  uint32_t f = __builtin_amdgcn_alignbit(hi, lo, 29);  // 8-bit exponent | top 23 mantissa bits
+  f |= (lo & 0x1FFFFFFFu) ? 1u : 0u;
+  return __uint_as_float(f);
+}
+
+// Exact NVFP4 element codes of 16 values: RNE(|x| / S) with R = 1/S correctly rounded in
+// float64 (R = 0 when S = 0 gives sign-only codes).  A float64 product |x| R lies within
+// 2^-52 (relative) of the real quotient, every non-midpoint quotient is at least 2^-33
+// away from a midpoint, and a midpoint quotient is recovered exactly, so the decisions
+// equal those of the exact quotient.
+__device__ __forceinline__ uint2 nvfp4_encode16_exact(const float* v, double R) {
+  float q[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    double a = fabs((double)v[i]) * R;
+    q[i] = copysignf(round_to_odd_f32(a), v[i]);
+  }
+  return e2m1_encode16(q, 1.0f);
+}
+
+// Fast NVFP4 element codes: RNE(fl32(x * E)) with E = fl32(1 / fl32(s_b s_t)).  Used where
+// the values themselves carry fp32 rounding (rotated or normalised inputs).
+__device__ __forceinline__ uint2 nvfp4_encode16_fast(const float* v, float E) {
+  float q[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q[i] = v[i] * E;
+  return e2m1_encode16(q, 1.0f);
+}
+
+// --------------------------------------------------------------------------- E4M3
+
+// E4M3 (OCP FP8 "FN") code of r >= 0: nearest finite value, ties to the even code,
+// saturating at 448 (code 0x7E).  Evaluated in float64 on a float64 argument.
+__device__ __forceinline__ uint32_t e4m3_rne(double r) {
+  if (r >= 448.0) return 0x7Eu;
+  if (r < 0x1p-6) return (uint32_t)rint(r * 512.0);     // subnormals: multiples of 2^-9
+  int e2;
+  (void)frexp(r, &e2);                                   // r = f 2^e2, f in [0.5, 1)
+  int E = e2 - 1;                                        // floor(log2 r), -6..8
+  uint32_t m = (uint32_t)rint(ldexp(r, 3 - E));          // 8..16 (16 carries into E + 1)
+  uint32_t code = (uint32_t)((E + 7) << 3) + m - 8u;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// NVFP4 block scale decision for block maximum amax under tensor scale s_t:
+// E4M3(amax / (6 s_t)) of the float64 quotient (6 s_t is exact in float64; the quotient
+// is within 2^-53 of the real one, which cannot move a decision: a non-tie argument is
+// at least 2^-33 away from an E4M3 midpoint and a tie divides exactly).
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float s_t) {
+  if (!(s_t > 0.0f)) return 0u;
+  return e4m3_rne((double)amax / (6.0 * (double)s_t));
+}
+
+// --------------------------------------------------------------------------- E8M0
+
+// MX scale code of a block maximum: floor(log2 amax) - 2 + 127, clamped to [0, 254];
+// 0 for an all-zero block.
+__device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
+  if (!(amax > 0.0f)) return 0u;
+  int e2;
+  (void)frexpf(amax, &e2);                   // amax = f 2^e2, f in [0.5, 1)
+  int e = e2 - 1 - 2;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return (uint32_t)(e + 127);
+}
+
+// 2^(code - 127) as a binary32 (code 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+}
+
+// --------------------------------------------------------------------------- reductions
+
+template <int N>
+__device__ __forceinline__ float absmax(const float* v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  return m;
+}
+
+__device__ __forceinline__ float wave_sum(float s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  return s;
+}
+
+// Running maximum of non-negative floats through their bit patterns (monotone for >= 0).
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+}  // namespace fp4dev

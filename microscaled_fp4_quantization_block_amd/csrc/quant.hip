@@ -1,0 +1,192 @@
+// Block-Hadamard + micro-scaled FP4 quantization and dequantization (NVFP4 and MXFP4).
+//
+// Work decomposition: one lane owns one 32-element chunk of a row (K % 32 == 0, so a
+// chunk never straddles rows and its codes are one 16-byte store).  A chunk holds whole
+// Hadamard blocks (16 or 32), one MXFP4 block or two NVFP4 blocks, so rotation, block
+// maxima, scale choice and encoding all stay in the lane's registers; the only
+// cross-lane step is the per-tensor maximum of NVFP4 (a wave reduction and one atomic
+// per wave, in a separate pass before the quantization launch).
+//
+// Sources: MR-GPTQ abstract (hyper.ai, Résumé) for block Hadamard before MXFP4 / NVFP4
+// quantization and online activation rotation; ARCQuant summary (gist.science, Énoncé du
+// Problème) for NVFP4 blocks of 16.
+#include "fp4_device.hpp"
+#include "fp4_internal.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kTensorDivisor = 2688.0f;   // largest E4M3 scale (448) x largest E2M1 value (6)
+
+template <int DT>
+__device__ __forceinline__ void load_chunk(const void* x, int64_t chunk, float* v) {
+  if constexpr (DT == fp4impl::DT_BF16)
+    load_bf16<32>(reinterpret_cast<const uint16_t*>(x) + chunk * 32, v);
+  else
+    load_f32<32>(reinterpret_cast<const float*>(x) + chunk * 32, v);
+}
+
+__global__ void k_zero_scalar(float* p) { *p = 0.0f; }
+
+// s_t = fl32(amax / 2688), in place (correctly rounded fp32 division).
+__global__ void k_finalize_tensor_scale(float* p) { *p = *p / kTensorDivisor; }
+
+// Per-tensor maximum of |H x| (running atomic max into *amax, which starts at 0).
+template <int DT, int H>
+__global__ void __launch_bounds__(kThreads) k_amax(const void* x, int64_t nchunks, float* amax) {
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float m = 0.0f;
+  if (c < nchunks) {
+    float v[32];
+    load_chunk<DT>(x, c, v);
+    block_hadamard<32, H>(v);
+    m = absmax<32>(v);
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomic_max_nonneg(amax, m);
+}
+
+template <int DT, int H>
+__global__ void __launch_bounds__(kThreads)
+k_quant_mx(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales, float* dbg) {
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= nchunks) return;
+  float v[32];
+  load_chunk<DT>(x, c, v);
+  block_hadamard<32, H>(v);
+  if (dbg) store_f32<32>(dbg + c * 32, v);
+  uint32_t e = e8m0_from_amax(absmax<32>(v));
+  reinterpret_cast<uint4*>(codes)[c] = e2m1_encode32(v, e8m0_value(e));
+  scales[c] = (uint8_t)e;
+}
+
+// NVFP4: two 16-blocks per chunk.  Unrotated input takes the exact element decision;
+// rotated input (already fp32-rounded) the fast one.
+template <int DT, int H>
+__global__ void __launch_bounds__(kThreads)
+k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
+           const float* tensor_scale, float* dbg) {
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= nchunks) return;
+  const float s_t = *tensor_scale;
+  float v[32];
+  load_chunk<DT>(x, c, v);
+  block_hadamard<32, H>(v);
+  if (dbg) store_f32<32>(dbg + c * 32, v);
+  uint2 w[2];
+  uint32_t sb[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    sb[b] = nvfp4_block_scale(absmax<16>(v + 16 * b), s_t);
+    if constexpr (H == 0) {
+      double S = (double)e4m3_value(sb[b]) * (double)s_t;     // exact
+      double R = S > 0.0 ? 1.0 / S : 0.0;
+      w[b] = nvfp4_encode16_exact(v + 16 * b, R);
+    } else {
+      float S32 = e4m3_value(sb[b]) * s_t;
+      float E = S32 > 0.0f ? 1.0f / S32 : 0.0f;
+      w[b] = nvfp4_encode16_fast(v + 16 * b, E);
+    }
+  }
+  reinterpret_cast<uint4*>(codes)[c] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
+  reinterpret_cast<uint16_t*>(scales)[c] = (uint16_t)(sb[0] | (sb[1] << 8));
+}
+
+// Dequantization: fl32(V s_b s_t) (NVFP4) or V 2^(e-127) (MXFP4), optional H, store.
+template <int FMT, int H, int OUT>
+__global__ void __launch_bounds__(kThreads)
+k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t nchunks,
+          void* y) {
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= nchunks) return;
+  uint4 w = reinterpret_cast<const uint4*>(codes)[c];
+  uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float v[32];
+  if constexpr (FMT == fp4impl::FMT_MX) {
+    float sc = e8m0_value(scales[c]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e2m1_decode8(ws[i], sc, v + 8 * i);
+  } else {
+    const float s_t = *tensor_scale;
+    uint32_t sb2 = reinterpret_cast<const uint16_t*>(scales)[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e2m1_decode8(ws[i], 1.0f, v + 8 * i);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float sb = e4m3_value((sb2 >> (8 * b)) & 0xFFu);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * b + i] = (v[16 * b + i] * sb) * s_t;   // V s_b exact
+    }
+  }
+  block_hadamard<32, H>(v);
+  if constexpr (OUT == fp4impl::DT_F32)
+    store_f32<32>(reinterpret_cast<float*>(y) + c * 32, v);
+  else
+    store_bf16<32>(reinterpret_cast<uint16_t*>(y) + c * 32, v);
+}
+
+inline dim3 grid_for(int64_t nchunks) { return dim3((unsigned)((nchunks + kThreads - 1) / kThreads)); }
+
+template <int DT, int H>
+hipError_t quantize_t(const void* x, int64_t nchunks, int fmt, uint8_t* codes, uint8_t* scales,
+                      float* ts, bool compute, float* dbg, hipStream_t st) {
+  dim3 g = grid_for(nchunks), b(kThreads);
+  if (fmt == fp4impl::FMT_MX) {
+    if (nchunks) k_quant_mx<DT, H><<<g, b, 0, st>>>(x, nchunks, codes, scales, dbg);
+    return hipGetLastError();
+  }
+  if (compute) {
+    k_zero_scalar<<<1, 1, 0, st>>>(ts);
+    if (nchunks) k_amax<DT, H><<<g, b, 0, st>>>(x, nchunks, ts);
+    k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
+  }
+  if (nchunks) k_quant_nv<DT, H><<<g, b, 0, st>>>(x, nchunks, codes, scales, ts, dbg);
+  return hipGetLastError();
+}
+
+template <int FMT, int H>
+hipError_t dequant_t(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t nchunks,
+                     void* y, int dt, hipStream_t st) {
+  if (!nchunks) return hipSuccess;
+  dim3 g = grid_for(nchunks), b(kThreads);
+  if (dt == fp4impl::DT_F32)
+    k_dequant<FMT, H, fp4impl::DT_F32><<<g, b, 0, st>>>(codes, scales, ts, nchunks, y);
+  else
+    k_dequant<FMT, H, fp4impl::DT_BF16><<<g, b, 0, st>>>(codes, scales, ts, nchunks, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace fp4impl {
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t M, int64_t K, int fmt, int hadamard,
+                           uint8_t* codes, uint8_t* scales, float* ts, bool compute, float* dbg,
+                           hipStream_t st) {
+  int64_t n = M * K / 32;
+  if (dtype == DT_BF16) {
+    if (hadamard == 0) return quantize_t<DT_BF16, 0>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+    if (hadamard == 16) return quantize_t<DT_BF16, 16>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+    return quantize_t<DT_BF16, 32>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+  }
+  if (hadamard == 0) return quantize_t<DT_F32, 0>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+  if (hadamard == 16) return quantize_t<DT_F32, 16>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+  return quantize_t<DT_F32, 32>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t M,
+                             int64_t K, int fmt, int hadamard, void* y, int dt, hipStream_t st) {
+  int64_t n = M * K / 32;
+  if (fmt == FMT_MX) {
+    if (hadamard == 0) return dequant_t<FMT_MX, 0>(codes, scales, ts, n, y, dt, st);
+    if (hadamard == 16) return dequant_t<FMT_MX, 16>(codes, scales, ts, n, y, dt, st);
+    return dequant_t<FMT_MX, 32>(codes, scales, ts, n, y, dt, st);
+  }
+  if (hadamard == 0) return dequant_t<FMT_NV, 0>(codes, scales, ts, n, y, dt, st);
+  if (hadamard == 16) return dequant_t<FMT_NV, 16>(codes, scales, ts, n, y, dt, st);
+  return dequant_t<FMT_NV, 32>(codes, scales, ts, n, y, dt, st);
+}
+
+}  // namespace fp4impl

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI: the library loads, exports every function include/fp4.h
+declares, and rejects invalid arguments before any HIP call (no compute happens here, so
+these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from microscaled_fp4_quantization_block_amd import binding as B
+from oracle import dualscale
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(B.library_path()),
+                               reason="libfp4.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in syms, name
+    L = B.lib()
+    for name in _declared():
+        assert hasattr(L, name)
+
+
+@needs_lib
+def test_status_strings():
+    L = B.lib()
+    for code, name in B._STATUS.items():
+        assert L.fp4_status_str(code).decode() == name
+    assert L.fp4_status_str(99).decode() == "FP4_E_UNKNOWN"
+
+
+@needs_lib
+def test_pack_bytes_matches_layout():
+    L = B.lib()
+    for M, K in [(1, 128), (3, 384), (8192, 8192), (7, 1024)]:
+        assert L.fp4_pack_bytes(M, K) == dualscale.layout(M, K)["total"]
+    assert L.fp4_pack_bytes(4, 100) == 0 and L.fp4_pack_bytes(-1, 128) == 0
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+MIS = 0x10008    # 8-byte aligned only
+
+
+def _status(fn, *args):
+    L = B.lib()
+    s = getattr(L, fn)(*args)
+    return s, L.fp4_last_error().decode()
+
+
+@needs_lib
+@pytest.mark.parametrize("args,want", [
+    ((FAKE, 1, 4, 33, 1, 0, FAKE, FAKE, None, 0, None, None), 2),       # K not a multiple of 32
+    ((FAKE, 1, -1, 32, 1, 0, FAKE, FAKE, None, 0, None, None), 2),      # negative M
+    ((FAKE, 1, 4, 32, 1, 8, FAKE, FAKE, None, 0, None, None), 4),       # unsupported rotation
+    ((FAKE, 1, 4, 32, 2, 0, FAKE, FAKE, None, 0, None, None), 4),       # unknown format
+    ((FAKE, 7, 4, 32, 1, 0, FAKE, FAKE, None, 0, None, None), 4),       # unknown dtype
+    ((FAKE, 1, 4, 32, 0, 0, FAKE, FAKE, None, 0, None, None), 1),       # NVFP4 without tensor scale
+    ((FAKE, 1, 4, 32, 1, 0, FAKE, FAKE, FAKE, 0, None, None), 4),       # MXFP4 with a tensor scale
+    ((None, 1, 4, 32, 1, 0, FAKE, FAKE, None, 0, None, None), 1),       # null input
+    ((MIS, 1, 4, 32, 1, 0, FAKE, FAKE, None, 0, None, None), 3),        # misaligned input
+    ((FAKE, 1, 4, 32, 1, 0, FAKE, FAKE + 2, None, 0, None, None), 3),   # misaligned scales
+])
+def test_quantize_validation(args, want):
+    s, msg = _status("fp4_quantize", *args)
+    assert s == want and msg.startswith("fp4_quantize")
+
+
+@needs_lib
+def test_other_entry_points_validation():
+    assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 48, 1, 0, FAKE, 0, None)[0] == 2
+    assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 64, 0, 0, FAKE, 0, None)[0] == 1
+    assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 64, 1, 64, FAKE, 0, None)[0] == 4
+    args = [FAKE, 4, 64, None, ctypes.c_float(1e-6), FAKE, 16, FAKE, FAKE, FAKE, 0, None, None]
+    bad = list(args); bad[6] = 24                                      # S not a multiple of 16
+    assert _status("fp4_residual_quantize", *bad)[0] == 2
+    bad = list(args); bad[6] = 80                                      # S > K
+    assert _status("fp4_residual_quantize", *bad)[0] == 2
+    bad = list(args); bad[5] = None                                    # no permutation
+    assert _status("fp4_residual_quantize", *bad)[0] == 1
+    bad = list(args); bad[2] = 32768                                   # K beyond the LDS row
+    assert _status("fp4_residual_quantize", *bad)[0] == 2
+    assert _status("fp4_pack", FAKE, 4, 100, FAKE, None, None)[0] == 2
+    assert _status("fp4_pack", FAKE, 4, 128, FAKE + 16, None, None)[0] == 3
+    assert _status("fp4_unpack", None, 4, 128, FAKE, None)[0] == 1
+    assert _status("fp4_gemm", FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 1, None)[0] == 2
+    assert _status("fp4_gemm", FAKE, FAKE, FAKE, FAKE, 4, 4, 0, FAKE, 1, None)[0] == 2
+    assert _status("fp4_gemm", FAKE, None, FAKE, FAKE, 4, 4, 128, FAKE, 1, None)[0] == 1
+    assert _status("fp4_gemm", FAKE, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 3, None)[0] == 4
+
+
+@needs_lib
+def test_empty_shapes_are_no_ops():
+    # M = 0 returns OK without touching the (null) buffers or the GPU
+    assert _status("fp4_quantize", None, 1, 0, 64, 1, 32, None, None, None, 0, None, None)[0] == 0
+    assert _status("fp4_dequantize", None, None, None, 0, 64, 1, 0, None, 0, None)[0] == 0
+    assert _status("fp4_pack", None, 0, 128, None, None, None)[0] == 0
+    assert _status("fp4_gemm", None, None, None, None, 0, 5, 128, None, 1, None)[0] == 0

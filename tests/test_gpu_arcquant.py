@@ -1,0 +1,86 @@
+"""GPU parity of the ARCQuant fused kernel (RMSNorm + reorder + primary / residual NVFP4)."""
+import numpy as np
+import pytest
+import torch
+
+import microscaled_fp4_quantization_block_amd as fp4
+from microscaled_fp4_quantization_block_amd import workloads as W
+from oracle import arcquant, formats as F
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _check_arc(xt, perm, S, gamma=None, eps=1e-6, rows=None, given=None):
+    M, K = xt.shape
+    x = xt.to(DEV)
+    dbg = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    g = None if gamma is None else torch.from_numpy(gamma.astype(np.float32)).to(DEV)
+    ts = None if given is None else torch.tensor([given], dtype=torch.float32, device=DEV)
+    codes, scales, ts = fp4.fp4_residual_quantize(
+        x, torch.from_numpy(perm.astype(np.int32)).to(DEV), S, gamma=g, eps=eps, tensor_scale=ts,
+        mode="compute" if given is None else "given", dbg_normed=dbg)
+    rows = np.arange(M) if rows is None else rows
+    xv = W.values(xt)
+    gam = None if gamma is None else gamma.astype(np.float32).astype(np.float64)
+    gst = _np(ts)[0]
+    if given is None:
+        full = arcquant.rmsnorm(xv, gam, eps)
+        P.assert_rel(gst, F.to_f32(np.max(np.abs(full)) / 2688.0), what="tensor scale")
+    else:
+        assert gst == np.float32(given)
+    xr = xv[rows]
+    gc = F.unpack_nibbles(_np(codes)[rows])
+    gs = _np(scales)[rows]
+    nb = K // 16
+    base = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst)
+    P.assert_values_close(_np(dbg)[rows], base["z"], K, what="normalized, reordered values")
+    P.check_e4m3_scales(gs[:, :nb], base["primary"]["scales"], base["primary"]["scale_arg"], what="primary scales")
+    c1 = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst, primary_scales=gs[:, :nb])
+    n = P.check_e2m1_codes(gc[:, :K], c1["primary"]["codes"], c1["primary"]["elem_arg"], c1["z"], 16,
+                           what="primary codes")
+    c2 = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst, primary_scales=gs[:, :nb],
+                           primary_codes=gc[:, :K])
+    if S:
+        P.check_e4m3_scales(gs[:, nb:], c2["residual"]["scales"], c2["residual"]["scale_arg"],
+                            what="residual scales")
+        c3 = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst, primary_scales=gs[:, :nb],
+                               primary_codes=gc[:, :K], residual_scales=gs[:, nb:])
+        n += P.check_e2m1_codes(gc[:, K:], c3["residual"]["codes"], c3["residual"]["elem_arg"],
+                                c3["residual_value"], 16, what="residual codes")
+    return n
+
+
+@pytest.mark.parametrize("M,K,S", [(1, 16, 16), (7, 128, 32), (33, 512, 0), (130, 1024, 256)])
+def test_arcquant_small(M, K, S):
+    print(f"arcquant M={M} K={K} S={S}", flush=True)
+    rng = np.random.default_rng(M * 31 + K)
+    x = rng.standard_normal((M, K))
+    x[:, rng.choice(K, max(1, K // 64), replace=False)] *= 30
+    xt = W.to_bf16(x)
+    perm = W.calibration_order(xt)
+    _check_arc(xt, perm, S)
+
+
+def test_arcquant_gamma_given_scale_and_random_perm():
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((50, 256))
+    xt = W.to_bf16(x)
+    perm = rng.permutation(256).astype(np.int32)
+    gamma = rng.uniform(0.5, 1.5, 256)
+    _check_arc(xt, perm, 64, gamma=gamma, eps=1e-5, given=0.0021)
+
+
+def test_arcquant_config_full_size():
+    """bf16 4096 x 4096 N(0,1), 64 outlier channels x30, S = 256 -> K+S = 4352, sampled rows."""
+    print("arcquant 4096x4096 seed 4 S=256", flush=True)
+    xt = W.arcquant_input()
+    perm = W.calibration_order(xt)
+    rows = W.seeded_rows(4096, 64, 40)
+    n = _check_arc(xt, perm, 256, rows=rows)
+    print(f"  boundary-tolerated code differences: {n}", flush=True)

@@ -1,0 +1,70 @@
+"""GPU parity of the dual-scale FP4 pack / unpack (two-level FWHT 16 x 8) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import microscaled_fp4_quantization_block_amd as fp4
+from microscaled_fp4_quantization_block_amd import workloads as W
+from oracle import dualscale, formats as F
+from oracle.hadamard import two_level_128
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _check_pack(xt, rows=None):
+    M, K = xt.shape
+    x = xt.to(DEV)
+    dbg = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    packed = fp4.fp4_pack(x, dbg_rotated=dbg)
+    y = fp4.fp4_unpack(packed, M, K)
+    assert packed.numel() == dualscale.layout(M, K)["total"] == fp4.fp4_pack_bytes(M, K)
+    buf = _np(packed)
+    codes, sm, sg = dualscale.split(buf, M, K)
+    rows = np.arange(M) if rows is None else rows
+    xv = W.values(xt)[rows]
+    ref = dualscale.pack_values(xv)
+    P.assert_values_close(_np(dbg)[rows], ref["y"], 128, what="two-level FWHT")
+    P.assert_rel(sg[rows], F.to_f32(ref["amax_g"] / 2688.0), what="group scales")
+    c1 = dualscale.pack_values(xv, group_scales=sg[rows])
+    P.check_e4m3_scales(sm[rows], c1["micro_scales"], c1["scale_arg"], what="micro scales")
+    c2 = dualscale.pack_values(xv, group_scales=sg[rows], micro_scales=sm[rows])
+    n = P.check_e2m1_codes(codes[rows], c2["codes"], c2["elem_arg"], c2["y"], 16)
+    # unpack of the GPU's own message: fl32(V s_m s_g), two-level FWHT, one bf16 rounding
+    want = two_level_128(dualscale.dequantized(codes[rows], sm[rows], sg[rows]))
+    P.assert_bf16_close(W.values(y.cpu())[rows], want, 128)
+    return n
+
+
+@pytest.mark.parametrize("shape", [(4, 128), (3, 384), (65, 1024)])
+def test_pack_small(shape):
+    print(f"pack {shape}", flush=True)
+    rng = np.random.default_rng(shape[0] + shape[1])
+    x = rng.standard_t(4, shape)
+    x[0, :128] = 2.0                      # constant group: exact zeros after the FWHT
+    if shape[0] > 1:
+        x[1, :128] = 0.0                  # all-zero group
+    _check_pack(W.to_bf16(x))
+
+
+def test_pack_config_full_size():
+    """bf16 8192 x 8192 Student-t(4), sampled rows."""
+    print("pack 8192x8192 Student-t(4) seed 3", flush=True)
+    x = W.student_t_input()
+    rows = W.seeded_rows(8192, 48, 30)
+    n = _check_pack(x, rows)
+    print(f"  boundary-tolerated code differences: {n}", flush=True)
+
+
+def test_pack_empty_and_deterministic():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    fp4.fp4_pack(x)
+    xt = W.to_bf16(np.random.default_rng(3).standard_t(4, (40, 512))).to(DEV)
+    a = _np(fp4.fp4_pack(xt))
+    b = _np(fp4.fp4_pack(xt))
+    assert np.array_equal(a, b)

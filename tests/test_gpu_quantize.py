@@ -1,0 +1,211 @@
+"""GPU parity of fp4_quantize / fp4_dequantize (NVFP4 and MXFP4, with and without block
+Hadamard rotation) against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import microscaled_fp4_quantization_block_amd as fp4
+from microscaled_fp4_quantization_block_amd import workloads as W
+from oracle import formats as F, hadamard as H, mxfp4, nvfp4
+from tests import parity as P
+from tests.test_oracle_quant import _mx_tie_rows, _nvfp4_tie_tensor
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _vals(t):
+    return W.values(t.cpu())
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------- NVFP4 exact
+
+def _nvfp4_exact_case(x_cpu, dtype_out=torch.float32):
+    x = x_cpu.to(DEV)
+    codes, scales, ts = fp4.fp4_quantize(x, "nvfp4", 0)
+    ref = nvfp4.quantize(_vals(x_cpu))
+    assert _np(ts)[0].tobytes() == np.float32(ref["tensor_scale"]).tobytes()
+    assert np.array_equal(_np(scales), ref["scales"])
+    assert np.array_equal(_np(codes), ref["packed"])
+    y = fp4.fp4_dequantize(codes, scales, ts, "nvfp4", 0, dtype_out)
+    want = nvfp4.dequantize(ref["packed"], ref["scales"], ref["tensor_scale"])
+    if dtype_out == torch.float32:
+        assert np.array_equal(_np(y), want.astype(np.float32))
+    else:
+        bits = _np(y.view(torch.int16)).view(np.uint16)
+        assert np.array_equal(bits, F.f32_to_bf16_bits(want.astype(np.float32)))
+    return ref
+
+
+def test_nvfp4_roundtrip_config_exact():
+    _log("nvfp4 roundtrip fp32 256x1024 seed 1")
+    x = W.nvfp4_roundtrip_input()
+    _nvfp4_exact_case(x)
+    _nvfp4_exact_case(x, torch.bfloat16)
+
+
+def test_nvfp4_exact_ties_and_wide_range():
+    _log("nvfp4 ties")
+    t = torch.from_numpy(_nvfp4_tie_tensor())
+    _nvfp4_exact_case(t)
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((33, 96)) * np.exp(rng.uniform(-25, 5, (33, 96)))).astype(np.float32)
+    x[3, 32:64] = 0.0
+    x[4, :16] = -0.0
+    _log("nvfp4 wide range 33x96")
+    _nvfp4_exact_case(torch.from_numpy(x))
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (5, 64), (257, 96), (3, 4096)])
+def test_nvfp4_bf16_shapes_exact(shape):
+    _log(f"nvfp4 bf16 {shape}")
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    x = W.to_bf16(rng.standard_normal(shape) * 3)
+    _nvfp4_exact_case(x)
+
+
+def test_nvfp4_given_scale_exact():
+    rng = np.random.default_rng(6)
+    x = torch.from_numpy(rng.standard_normal((64, 256)).astype(np.float32))
+    ts = torch.tensor([0.0123], dtype=torch.float32, device=DEV)
+    codes, scales, _ = fp4.fp4_quantize(x.to(DEV), "nvfp4", 0, tensor_scale=ts, mode="given")
+    ref = nvfp4.quantize(_vals(x), tensor_scale_value=np.float32(0.0123))
+    assert np.array_equal(_np(scales), ref["scales"]) and np.array_equal(_np(codes), ref["packed"])
+    assert _np(ts)[0] == np.float32(0.0123)
+
+
+def test_empty_inputs():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    codes, scales, ts = fp4.fp4_quantize(x, "nvfp4", 0)
+    torch.cuda.synchronize()
+    assert codes.numel() == 0 and float(ts.cpu()[0]) == 0.0
+    codes, scales, _ = fp4.fp4_quantize(x, "mxfp4", 32)
+    assert codes.numel() == 0
+
+
+# ----------------------------------------------------------------------------- MXFP4 exact
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_mxfp4_unrotated_exact(dtype):
+    _log(f"mxfp4 unrotated {dtype}")
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((129, 160)) * np.exp(rng.uniform(-30, 30, (129, 1))))
+    x[0] = 0.0
+    xt = torch.from_numpy(x.astype(np.float32)).to(dtype)
+    xt[1, :32] = torch.from_numpy(_mx_tie_rows()[0]).to(dtype)
+    codes, scales, _ = fp4.fp4_quantize(xt.to(DEV), "mxfp4", 0)
+    ref = mxfp4.quantize(_vals(xt))
+    assert np.array_equal(_np(scales), ref["scales"])
+    assert np.array_equal(_np(codes), ref["packed"])
+    y = fp4.fp4_dequantize(codes, scales, None, "mxfp4", 0, torch.float32)
+    want = mxfp4.dequantize(ref["packed"], ref["scales"])
+    assert np.array_equal(_np(y).astype(np.float64), want.astype(np.float32).astype(np.float64))
+
+
+def test_mxfp4_tie_rows_exact():
+    t = torch.from_numpy(_mx_tie_rows())
+    codes, scales, _ = fp4.fp4_quantize(t.to(DEV), "mxfp4", 0)
+    ref = mxfp4.quantize(_vals(t))
+    assert np.array_equal(_np(codes), ref["packed"]) and np.array_equal(_np(scales), ref["scales"])
+
+
+# ----------------------------------------------------------------------------- rotated
+
+def _check_mx_rotated(x_cpu, h, rows=None):
+    x = x_cpu.to(DEV)
+    M, K = x.shape
+    dbg = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    codes, scales, _ = fp4.fp4_quantize(x, "mxfp4", h, dbg_rotated=dbg)
+    y_bf16 = fp4.fp4_dequantize(codes, scales, None, "mxfp4", h, torch.bfloat16)
+    y_f32 = fp4.fp4_dequantize(codes, scales, None, "mxfp4", 0, torch.float32)
+    rows = np.arange(M) if rows is None else rows
+    xv = _vals(x_cpu)[rows]
+    g_codes = F.unpack_nibbles(_np(codes)[rows])
+    g_scales = _np(scales)[rows]
+    ref = mxfp4.quantize(xv, hadamard=h)
+    P.assert_values_close(_np(dbg)[rows], ref["y"], 32, what="rotated values")
+    P.check_e8m0_scales(g_scales, ref["scales"], ref["amax"])
+    cond = mxfp4.quantize(xv, hadamard=h, block_scales=g_scales)
+    n = P.check_e2m1_codes(g_codes, cond["codes"], cond["elem_arg"], cond["y"], 32)
+    # dequantization of the GPU's own codes is exact without rotation ...
+    want = mxfp4.dequantize(_np(codes)[rows], g_scales)
+    assert np.array_equal(_np(y_f32)[rows].astype(np.float64), want)
+    # ... and one bf16 rounding of the fp32 inverse rotation with it
+    want_h = mxfp4.dequantize(_np(codes)[rows], g_scales, inverse_hadamard=h)
+    P.assert_bf16_close(_vals(y_bf16.cpu())[rows], want_h, 32)
+    return n
+
+
+@pytest.mark.parametrize("h", [16, 32])
+def test_mxfp4_rotated_small(h):
+    _log(f"mxfp4 H{h} small")
+    rng = np.random.default_rng(h)
+    x = rng.standard_normal((37, 224))
+    x[:, 3] *= 50
+    x[5] = 1.0                                   # constant rows: exact zeros after H
+    _check_mx_rotated(W.to_bf16(x), h)
+
+
+def test_mxfp4_h32_config_full_size():
+    """4096 x 4096 bf16 with 41 outlier channels x50, Hadamard 32, sampled rows."""
+    _log("mxfp4 H32 4096x4096 seed 2")
+    x = W.mxfp4_h32_input()
+    rows = W.seeded_rows(4096, 96, 20)
+    n = _check_mx_rotated(x, 32, rows)
+    _log(f"  boundary-tolerated code differences: {n}")
+
+
+@pytest.mark.parametrize("h", [16, 32])
+def test_nvfp4_rotated(h):
+    _log(f"nvfp4 H{h}")
+    rng = np.random.default_rng(100 + h)
+    x = rng.standard_normal((65, 256))
+    x[:, 7] *= 40
+    xt = W.to_bf16(x)
+    xg = xt.to(DEV)
+    dbg = torch.empty(x.shape, dtype=torch.float32, device=DEV)
+    codes, scales, ts = fp4.fp4_quantize(xg, "nvfp4", h, dbg_rotated=dbg)
+    xv = _vals(xt)
+    ref = nvfp4.quantize(xv, hadamard=h)
+    P.assert_values_close(_np(dbg), ref["y"], h, what="rotated values")
+    gst = _np(ts)[0]
+    P.assert_rel(gst, ref["tensor_scale"], what="tensor scale")
+    c1 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst)
+    P.check_e4m3_scales(_np(scales), c1["scales"], c1["scale_arg"])
+    c2 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst, block_scales=_np(scales))
+    P.check_e2m1_codes(F.unpack_nibbles(_np(codes)), c2["codes"], c2["elem_arg"], c2["y"], 16)
+    y = fp4.fp4_dequantize(codes, scales, ts, "nvfp4", h, torch.float32)
+    want = nvfp4.dequantize(_np(codes), _np(scales), gst, inverse_hadamard=h)
+    P.assert_values_close(_np(y), want, h, what="dequantized + inverse H")
+
+
+# ----------------------------------------------------------------------------- robustness
+
+def test_determinism_and_poisoned_outputs():
+    x = W.to_bf16(np.random.default_rng(9).standard_normal((300, 512))).to(DEV)
+    outs = []
+    for fill in (0xAB, 0x00):
+        cc = torch.full((300, 256), fill, dtype=torch.uint8, device=DEV)
+        s = torch.full((300, 16), fill, dtype=torch.uint8, device=DEV)
+        fp4.fp4_quantize(x, "mxfp4", 32, codes=cc, scales=s)
+        outs.append((_np(cc).copy(), _np(s).copy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_canary_after_outputs():
+    M, K = 77, 224
+    x = W.to_bf16(np.random.default_rng(10).standard_normal((M, K))).to(DEV)
+    buf = torch.full((M * K // 2 + 4096,), 0x5A, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((M * K // 16 + 4096,), 0x5A, dtype=torch.uint8, device=DEV)
+    codes = buf[:M * K // 2].view(M, K // 2)
+    scales = sbuf[:M * K // 16].view(M, K // 16)
+    fp4.fp4_quantize(x, "nvfp4", 0, codes=codes, scales=scales)
+    assert (_np(buf)[M * K // 2:] == 0x5A).all() and (_np(sbuf)[M * K // 16:] == 0x5A).all()
