@@ -8,18 +8,36 @@
 // Design (gfx950):
 // - v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 (cbsz = blgp = 4) and one
 //   E8M0 scale per lane per operand: lane l supplies row (l % 32) of its operand, the
-//   32-element K block (l / 32) of the current 64-element step (16 bytes of codes), and
-//   that block's scale byte.  The product is computed as C^T = B A^T so that each lane
-//   ends up holding four consecutive output columns of one output row (an 8-byte bf16
-//   store) instead of four rows of one column.
-// - Workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 MFMA tiles, 256 fp32
-//   accumulators per lane), K step 256 elements = 128 bytes per row = one cache line.
-// - Global -> register prefetch of the next K step while the current one is multiplied
-//   out of LDS; LDS rows padded to 144 bytes so the 16-lane phases of a 16-byte LDS read
-//   hit distinct banks.
+//   32-element K block (l / 32) of the current 64-element sub-step (16 bytes of codes),
+//   and that block's scale byte.  The product is computed as C^T = B A^T so that each
+//   lane ends up holding four consecutive output columns of one output row (an 8-byte
+//   bf16 store) instead of four rows of one column.
+// - Workgroup tile 256 x 256, 8 waves in a 4 x 2 grid of 64 x 128 (2 x 4 MFMA tiles, 128
+//   fp32 accumulators per lane).  Two waves per SIMD: one wave's LDS reads and barrier
+//   waits hide behind the other's MFMAs.
+// - K advances in buffers of 256 elements: 128 code bytes per row (one cache line) per
+//   operand.  Codes go global -> LDS directly (buffer_load ... lds, 16 bytes per lane,
+//   eight lanes per row), double-buffered: buffer p + 2 is issued into the slot of
+//   buffer p right after the barrier that ends buffer p's reads, so each load has a whole
+//   buffer of MFMAs (64 per wave) to land.  Scales travel the same way in groups of 16
+//   bytes per row (512 K elements), double-buffered per group.  No VGPR staging, no LDS
+//   write instructions.
+// - Per buffer, one barrier, placed before the last 64-element sub-step: that sub-step's
+//   MFMAs run while the next buffer's first fragments and scales are read and the refill
+//   is issued.  The barrier is a bare s_barrier after an explicit wait for the wave's own
+//   loads; no memory fence, which would drain every load in flight.
+// - Each 128-byte LDS row holds its eight 16-byte chunks XOR-swizzled by (row / 2) % 8, so
+//   the sixteen lanes that share an LDS pass (one chunk of sixteen consecutive rows)
+//   touch sixteen distinct 16-byte bank groups.
+// - Buffer resources are built per tile: rows past M or N fall outside the resource and
+//   read as zero (never fault), and only feed outputs that are not stored.
 // - Tiles are assigned XCD-aware: consecutive workgroup ids land on different XCDs, so the
 //   id is remapped to give every XCD a contiguous band of tiles, walked in groups of 8
 //   tile-rows, keeping each XCD's L2 working set to a few A and B panels.
+// - When K is a multiple of 512, each tile starts its walk over K at a buffer offset set
+//   by its tile coordinates and wraps around: tiles that run together then read different
+//   K columns of their panels at any moment, which spreads the load over memory channels.
+//   Only the fp32 summation order changes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,15 +48,25 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BN = 256, BK = 256;      // BK in elements
-constexpr int ROWB = BK / 2;                      // code bytes per row per K step
-constexpr int LDS_STRIDE = ROWB + 16;             // padded LDS row
-constexpr int kThreads = 256;
-constexpr int kChunks = BM * ROWB / 16 / kThreads; // 16-byte chunks per thread per operand (8)
+constexpr int BM = 256, BN = 256;
+constexpr int BKP = 256;                           // K elements per LDS buffer ("pair" of 128-steps)
+constexpr int ROWB = BKP / 2;                      // code bytes per row per buffer (128, one line)
+constexpr int kCodeBytes = BM * ROWB;              // 32 KiB per operand per buffer
+constexpr int kBufBytes = 2 * kCodeBytes;          // A + B codes
+constexpr int kScaleRow = 16;                      // scale bytes per row per group (2 buffers = 512 K)
+constexpr int kScaleBytes = BM * kScaleRow;        // 4 KiB per operand per group
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
-constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kRsrcWord3 = 0x00020000;             // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kOOB = 0x80000000u;             // offset past every resource: reads 0
+
+// Wave arrangement: NW waves as WM x WN, each owning TI x TJ MFMA blocks of 32 x 32.
+template <int NW> struct Cfg;
+template <> struct Cfg<4> { static constexpr int WM = 2, WN = 2, TI = 4, TJ = 4; };
+template <> struct Cfg<8> { static constexpr int WM = 4, WN = 2, TI = 2, TJ = 4; };
 
 struct Tile { int m0, n0; };
 
@@ -58,133 +86,291 @@ __device__ __forceinline__ Tile tile_of(int id, int tiles_m, int tiles_n) {
   return t;
 }
 
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+// LDS slot of 16-byte chunk c of code row r: c ^ ((r / 2) % 8).  A 16-byte LDS read
+// serves 16 lanes per pass over 64 four-byte banks (256 bytes = two 128-byte rows); the
+// fragment reads of 16 consecutive rows at one chunk then touch 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Raw buffer descriptor over [base, base + bytes): stride 0, 32-bit data format.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
+}
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at lds + 16 lane
+// (one wait state between the M0 write and the load that reads it).
+// Written as one asm statement (M0 set and the load issued together; it has no register
+// results) so the compiler neither sees nor waits on the LDS write: every wait for these
+// loads is the explicit vmcnt(0) before a workgroup barrier.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, const uint8_t* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// Per-thread loader state.  Per buffer and operand, 32 code instructions (8 rows x 128
+// bytes = 1 KiB each) are split over the waves, QW = 32 / NW each; per scale group and
+// operand, 4 instructions (64 rows x 16 bytes), SW = 8 / NW per wave over both operands.
+template <int NW>
+struct Loader {
+  static constexpr int QW = 32 / NW;
+  static constexpr int SW = 8 / NW;
+  u32x4 rA, rB, rSA, rSB;   // buffer descriptors (wave-uniform, SGPRs)
+  uint32_t code_off[2];   // lane offset of instruction 0 (even) / 1 (odd); +8 q rows per q
+  uint32_t row_step;      // 8 rows in bytes
+  uint32_t scale_off[SW];
+  int wave;
+  int rot, np;            // starting buffer (even) and buffer count; rot = 0 unless K % 512 == 0
+};
+
+// Buffer that the tile processes at step p: p + rot, wrapped into [0, np).
+template <int NW>
+__device__ __forceinline__ int rotated(const Loader<NW>& L, int p) {
+  const int q = p + L.rot;
+  return q >= L.np ? q - L.np : q;
+}
+
+// Issue buffer p (K elements 256 p ..) of both operands into `dst`.  Code instruction g
+// fills bytes [g KiB, +1 KiB): lane l lands at byte 16 l = row 8 g + l / 8, slot l % 8,
+// holding global chunk (l % 8) ^ swz(row) (which depends on g only through g % 2).
+// `valid` false issues the instructions with every offset out of range (no memory
+// traffic), keeping the control flow straight.
+template <int NW>
+__device__ __forceinline__ void issue_codes(const Loader<NW>& L, int p, bool valid, uint8_t* dst) {
+  const int soff = rotated(L, p) * ROWB;
+#pragma unroll
+  for (int q = 0; q < Loader<NW>::QW; ++q) {
+    uint8_t* blk = dst + (Loader<NW>::QW * L.wave + q) * 1024;
+    const uint32_t off = valid ? L.code_off[q & 1] + (uint32_t)(q & ~1) * L.row_step : kOOB;
+    dma16(L.rA, blk, off, soff);
+    dma16(L.rB, blk + kCodeBytes, off, soff);
+  }
+}
+
+// Issue scale group h (16 scale bytes per row: K elements 512 h .., counted from the
+// tile's starting buffer) into `dst` ([A rows][16 B] then [B rows][16 B]); instruction t
+// covers rows 64 (t % 4) + l of operand t / 4.  rot is even, so a group never straddles
+// the wrap.
+template <int NW>
+__device__ __forceinline__ void issue_scales(const Loader<NW>& L, int h, bool valid, uint8_t* dst) {
+  const int soff = (rotated(L, 2 * h) >> 1) * kScaleRow;
+#pragma unroll
+  for (int q = 0; q < Loader<NW>::SW; ++q) {
+    const int t = Loader<NW>::SW * L.wave + q;
+    uint8_t* blk = dst + (t >> 2) * kScaleBytes + (t & 3) * 1024;
+    dma16((t >> 2) ? L.rSB : L.rSA, blk, valid ? L.scale_off[q] : kOOB, soff);
+  }
+}
+
+template <int NW>
+struct Frags {
+  v8i a[Cfg<NW>::TI], b[Cfg<NW>::TJ];
+};
+
+// Fragments of sub-step t (0..3, 64 K elements each) of the buffer `src`.
+template <int NW>
+__device__ __forceinline__ void read_codes(const uint8_t* src, int t, int wm, int wn, int r32,
+                                           int khalf, Frags<NW>& f) {
+  const int slot = ((2 * t + khalf) ^ swz(r32)) * 16;
+#pragma unroll
+  for (int j = 0; j < Cfg<NW>::TJ; ++j) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(src + kCodeBytes + (wn + 32 * j + r32) * ROWB + slot);
+    f.b[j] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg<NW>::TI; ++i) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(src + (wm + 32 * i + r32) * ROWB + slot);
+    f.a[i] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+  }
+}
+
+// The 8 scale bytes of buffer p (blocks 8 (p % 2) .. of its group) for this lane's rows.
+// For a buffer that ends after 128 elements (`half`), the scales of the four blocks past
+// the end are set to 2^-127 on both operands: whatever (finite) codes lie there then
+// contribute 2^-254 times at most 36, which is exactly zero in fp32.
+template <int NW>
+__device__ __forceinline__ void read_scales(const uint8_t* sgrp, int p, bool half, int wm, int wn,
+                                            int r32, u32x2 (&sa)[Cfg<NW>::TI], u32x2 (&sb)[Cfg<NW>::TJ]) {
+  const int off = 8 * (p & 1);
+#pragma unroll
+  for (int i = 0; i < Cfg<NW>::TI; ++i) {
+    sa[i] = *reinterpret_cast<const u32x2*>(sgrp + (wm + 32 * i + r32) * kScaleRow + off);
+    sa[i][1] = half ? 0u : sa[i][1];
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg<NW>::TJ; ++j) {
+    sb[j] = *reinterpret_cast<const u32x2*>(sgrp + kScaleBytes + (wn + 32 * j + r32) * kScaleRow + off);
+    sb[j][1] = half ? 0u : sb[j][1];
+  }
+}
+
+// MFMAs of sub-step t: the lane's scale byte is block 2 t + khalf of the buffer.
+template <int NW>
+__device__ __forceinline__ void mfma_substep(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], const Frags<NW>& f,
+                                             const u32x2 (&sa)[Cfg<NW>::TI], const u32x2 (&sb)[Cfg<NW>::TJ],
+                                             int t, int khalf) {
+  const int sh = 8 * (2 * (t & 1) + khalf);
+#pragma unroll
+  for (int i = 0; i < Cfg<NW>::TI; ++i) {
+    const int scale_a = (int)(sa[i][t >> 1] >> sh);
+#pragma unroll
+    for (int j = 0; j < Cfg<NW>::TJ; ++j) {
+      const int scale_b = (int)(sb[j][t >> 1] >> sh);
+      // C^T tile = B-rows x A-rows^T: instruction operand A <- B codes, operand B <- A codes
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 4, 4, 0,
+                                                                  scale_b, 0, scale_a);
+    }
+  }
+}
+
+// Interleave R LDS reads with F MFMAs in the current scheduling region: group k holds
+// one read and F / R MFMAs, one more for the first F % R groups.
+template <int k, int R, int F>
+__device__ __forceinline__ void interleave_groups() {
+  if constexpr (k < R) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, F / R + (k < F % R ? 1 : 0), 0);  // MFMA
+    interleave_groups<k + 1, R, F>();
+  }
+}
+template <int NW>
+__device__ __forceinline__ void interleave_reads() {
+  interleave_groups<0, Cfg<NW>::TI + Cfg<NW>::TJ, Cfg<NW>::TI * Cfg<NW>::TJ>();
+}
+
+// One buffer (4 sub-steps).  On entry f[0] holds sub-step 0 of buffer p (in `cur`) and
+// sa/sb its scales.  Sub-steps 0..2 each run their MFMAs while the next sub-step's
+// fragments are read.  Then every wave waits for its DMA of buffer p + 1 and meets the
+// barrier: buffer p + 1 is complete and every read of `cur` is done, so `cur` is refilled
+// with buffer p + 2 while sub-step 3 runs and the first fragments of buffer p + 1 are
+// read.  Steps with p even also refill `sgrp_refill` with the scale group that starts at
+// buffer p + 2.  Past the end the loads go out of range: they move no data but still
+// write zeros to LDS, into slots that are dead by then (`cur` after its last read, and a
+// scale slot whose group was last read two steps earlier).
+template <int NW, bool kRefillScales>
+__device__ __forceinline__ void run_buffer(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], Frags<NW> (&f)[2],
+                                           u32x2 (&sa)[Cfg<NW>::TI], u32x2 (&sb)[Cfg<NW>::TJ],
+                                           const Loader<NW>& L, int p, int np, bool ragged,
+                                           uint8_t* cur, const uint8_t* next,
+                                           uint8_t* sgrp_refill, const uint8_t* sgrp_next,
+                                           int wm, int wn, int r32, int khalf) {
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    read_codes<NW>(cur, t + 1, wm, wn, r32, khalf, f[(t + 1) & 1]);
+    mfma_substep<NW>(acc, f[t & 1], sa, sb, t, khalf);
+    interleave_reads<NW>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // own DMA of buffer p + 1 landed and own reads of `cur` done; then the workgroup
+  // barrier (no memory fence: the waits above are the ordering this step needs)
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  u32x2 na[Cfg<NW>::TI], nb[Cfg<NW>::TJ];
+  read_scales<NW>(sgrp_next, p + 1, ragged && p + 1 == np - 1, wm, wn, r32, na, nb);
+  read_codes<NW>(next, 0, wm, wn, r32, khalf, f[0]);
+  const int q = p + 2;
+  if constexpr (kRefillScales) issue_scales<NW>(L, q >> 1, q < np, sgrp_refill);
+  issue_codes<NW>(L, q, q < np, cur);
+  mfma_substep<NW>(acc, f[1], sa, sb, 3, khalf);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < Cfg<NW>::TI; ++i) sa[i] = na[i];
+#pragma unroll
+  for (int j = 0; j < Cfg<NW>::TJ; ++j) sb[j] = nb[j];
+}
+
+// The whole walk over K.  Code buffer p lives in c[p % 2] and scale group h in s[h % 2];
+// the loop is unrolled by four so that every access names its slot statically.  All four
+// slots arrive as restrict pointers of this one function, so the compiler knows for the
+// whole loop that a DMA into one slot never overlaps reads of another and adds no waits
+// of its own (the loop-carried DMA would otherwise cost a full drain per buffer).
+template <int NW>
+__device__ __forceinline__ void k_loop(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], const Loader<NW>& L, int np,
+                                       bool ragged, uint8_t* __restrict__ c0, uint8_t* __restrict__ c1,
+                                       uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, int wm, int wn,
+                                       int r32, int khalf) {
+  // prologue: buffers 0 and 1 and scale group 0 in flight
+  issue_scales<NW>(L, 0, true, s0);
+  issue_codes<NW>(L, 0, true, c0);
+  issue_codes<NW>(L, 1, np > 1, c1);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  Frags<NW> f[2];
+  u32x2 sa[Cfg<NW>::TI], sb[Cfg<NW>::TJ];
+  read_scales<NW>(s0, 0, ragged && np == 1, wm, wn, r32, sa, sb);
+  read_codes<NW>(c0, 0, wm, wn, r32, khalf, f[0]);
+  for (int p = 0; p < np; p += 4) {
+    run_buffer<NW, true>(acc, f, sa, sb, L, p, np, ragged, c0, c1, s1, s0, wm, wn, r32, khalf);
+    if (p + 1 < np) run_buffer<NW, false>(acc, f, sa, sb, L, p + 1, np, ragged, c1, c0, s0, s1, wm, wn, r32, khalf);
+    if (p + 2 < np) run_buffer<NW, true>(acc, f, sa, sb, L, p + 2, np, ragged, c0, c1, s0, s1, wm, wn, r32, khalf);
+    if (p + 3 < np) run_buffer<NW, false>(acc, f, sa, sb, L, p + 3, np, ragged, c1, c0, s1, s0, wm, wn, r32, khalf);
+  }
+}
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
        const uint8_t* __restrict__ SB, int M, int N, int K, void* __restrict__ C, int ctype) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[BN * LDS_STRIDE];
-  __shared__ uint2 sSA[BM];
-  __shared__ uint2 sSB[BN];
+  // device-only body (buffer resources and MFMA builtins have no host form)
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int TI = Cfg<NW>::TI, TJ = Cfg<NW>::TJ;
+  __shared__ __attribute__((aligned(1024))) uint8_t codes[2][kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t scales[2][2 * kScaleBytes];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
   const uint32_t rowbytes = (uint32_t)K / 2, rowscales = (uint32_t)K / 32;
-  const int nk = (K + BK - 1) / BK;
-  const bool ragged = (K % BK) != 0;              // last K step holds only 128 elements
+  const int np = (K + BKP - 1) / BKP;              // K % 128 == 0
+  const bool ragged = (K % BKP) != 0;              // last buffer holds 128 elements
 
-  // Buffer resources: out-of-range offsets read as 0 and never fault, so rows past M / N
-  // need no clamping (they only feed outputs that are never stored).
-  const uint32_t kOOB = 0x80000000u;
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(rowbytes * (uint32_t)M), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, (int)(rowbytes * (uint32_t)N), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)SA, 0, (int)(rowscales * (uint32_t)M), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)SB, 0, (int)(rowscales * (uint32_t)N), kRsrcWord3);
-
-  // loader mapping: chunk i of thread tid -> row (tid / 8) + 32 i, 16-byte column tid % 8
-  const int lrow = tid >> 3, lcol = (tid & 7) * 16;
-  uint32_t offA[kChunks], offB[kChunks];
+  Loader<NW> L;
+  {
+    const uint32_t rows_a = (uint32_t)min(BM, M - tile.m0), rows_b = (uint32_t)min(BN, N - tile.n0);
+    L.rA = make_rsrc(A + (size_t)tile.m0 * rowbytes, rows_a * rowbytes);
+    L.rB = make_rsrc(B + (size_t)tile.n0 * rowbytes, rows_b * rowbytes);
+    L.rSA = make_rsrc(SA + (size_t)tile.m0 * rowscales, rows_a * rowscales);
+    L.rSB = make_rsrc(SB + (size_t)tile.n0 * rowscales, rows_b * rowscales);
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int am = tile.m0 + lrow + 32 * i, bn = tile.n0 + lrow + 32 * i;
-    offA[i] = am < M ? (uint32_t)am * rowbytes + lcol : kOOB;
-    offB[i] = bn < N ? (uint32_t)bn * rowbytes + lcol : kOOB;
+    for (int q = 0; q < 2; ++q) {
+      const int row = 8 * (Loader<NW>::QW * wave + q) + (lane >> 3);
+      L.code_off[q] = (uint32_t)row * rowbytes + 16u * (uint32_t)((lane & 7) ^ swz(row));
+    }
+    L.row_step = 8u * rowbytes;
+#pragma unroll
+    for (int q = 0; q < Loader<NW>::SW; ++q) {
+      const int t = Loader<NW>::SW * wave + q;
+      L.scale_off[q] = (uint32_t)(64 * (t & 3) + lane) * rowscales;
+    }
+    L.wave = wave;
+    L.np = np;
+    L.rot = (K % (2 * BKP) == 0) ? (2 * (tile.m0 / BM + tile.n0 / BN)) % np : 0;
   }
-  const uint32_t offSA = tile.m0 + tid < M ? (uint32_t)(tile.m0 + tid) * rowscales : kOOB;
-  const uint32_t offSB = tile.n0 + tid < N ? (uint32_t)(tile.n0 + tid) * rowscales : kOOB;
 
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  u32x4 ra[kChunks], rb[kChunks];
-  u32x2 rsa, rsb;
-  auto gload = [&](int kb) {
-    const int soff = kb * ROWB;
+  const int wm = (wave / Cfg<NW>::WN) * (32 * TI), wn = (wave % Cfg<NW>::WN) * (32 * TJ);
+  const int r32 = lane & 31, khalf = lane >> 5;   // row within a 32-block, K block in a sub-step
+  v16f acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA[i], soff, 0);
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB[i], soff, 0);
-    }
-    rsa = __builtin_amdgcn_raw_buffer_load_b64(rSA, offSA, kb * (BK / 32), 0);
-    rsb = __builtin_amdgcn_raw_buffer_load_b64(rSB, offSB, kb * (BK / 32), 0);
-    if (ragged && kb == nk - 1) {                   // keep only the first 128 elements
-      if (lcol >= ROWB / 2) {
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) { ra[i] = u32x4{0, 0, 0, 0}; rb[i] = u32x4{0, 0, 0, 0}; }
-      }
-      rsa[1] = 0x7F7F7F7Fu;
-      rsb[1] = 0x7F7F7F7Fu;
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int row = lrow + 32 * i;
-      *reinterpret_cast<u32x4*>(sA + row * LDS_STRIDE + lcol) = ra[i];
-      *reinterpret_cast<u32x4*>(sB + row * LDS_STRIDE + lcol) = rb[i];
-    }
-    sSA[tid] = make_uint2(rsa[0], rsa[1]);
-    sSB[tid] = make_uint2(rsb[0], rsb[1]);
-  };
-
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
-  const int r32 = lane & 31, khalf = lane >> 5;     // row within a 32-tile, K block in a step
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
-    if (kb + 1 < nk) gload(kb + 1);
-    uint2 sa[4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = sSA[wm + 32 * i + r32];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = sSB[wn + 32 * j + r32];
-#pragma unroll
-    for (int s = 0; s < BK / 64; ++s) {
-      const int off = s * 32 + khalf * 16;
-      const int sh = 16 * (s & 1) + 8 * khalf;
-      v8i fb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 w = *reinterpret_cast<const uint4*>(sB + (wn + 32 * j + r32) * LDS_STRIDE + off);
-        fb[j] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 w = *reinterpret_cast<const uint4*>(sA + (wm + 32 * i + r32) * LDS_STRIDE + off);
-        const v8i fa = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-        const int scale_a = (int)(((s < 2) ? sa[i].x : sa[i].y) >> sh);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int scale_b = (int)(((s < 2) ? sb[j].x : sb[j].y) >> sh);
-          // C^T tile = B-rows x A-rows^T: instruction operand A <- B codes, operand B <- A codes
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fb[j], fa, acc[i][j], 4, 4, 0, scale_b, 0, scale_a);
-        }
-      }
-    }
-    __syncthreads();
-    if (kb + 1 < nk) {
-      lstore();
-      __syncthreads();
-    }
-  }
+  k_loop<NW>(acc, L, np, ragged, codes[0], codes[1], scales[0], scales[1], wm, wn, r32, khalf);
 
-  // epilogue: lane holds C[m][n0 .. n0+3] for m = row r32 of A-tile i, n0 = 8 g + 4 khalf in B-tile j
+  // epilogue: lane holds C[m][n0 .. n0+3] for m = row r32 of A-block i, n0 = 8 g + 4 khalf in B-block j
+  const bool vec_ok = (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TI; ++i) {
     const int m = tile.m0 + wm + 32 * i + r32;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TJ; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n0 = tile.n0 + wn + 32 * j + 8 * g + 4 * khalf;
@@ -192,7 +378,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
         const float c2 = acc[i][j][4 * g + 2], c3 = acc[i][j][4 * g + 3];
         if (ctype == fp4impl::DT_BF16) {
           uint16_t* cp = reinterpret_cast<uint16_t*>(C) + (int64_t)m * N + n0;
-          if (n0 + 3 < N && (N & 3) == 0) {
+          if (vec_ok && n0 + 3 < N) {
             *reinterpret_cast<uint2*>(cp) = make_uint2(fp4dev::pack_bf16x2(c0, c1), fp4dev::pack_bf16x2(c2, c3));
           } else {
             if (n0 < N) cp[0] = (uint16_t)fp4dev::bf16_bits_rne(c0);
@@ -202,7 +388,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
           }
         } else {
           float* cp = reinterpret_cast<float*>(C) + (int64_t)m * N + n0;
-          if (n0 + 3 < N && (N & 3) == 0) {
+          if (vec_ok && n0 + 3 < N) {
             *reinterpret_cast<float4*>(cp) = make_float4(c0, c1, c2, c3);
           } else {
             if (n0 < N) cp[0] = c0;
@@ -214,17 +400,23 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
       }
     }
   }
+#endif
 }
 
 }  // namespace
 
 namespace fp4impl {
 
+#ifndef FP4_GEMM_WAVES
+#define FP4_GEMM_WAVES 8
+#endif
+constexpr int kWaves = FP4_GEMM_WAVES;
+
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, void* c, int ctype, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  k_gemm<<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(a, sa, b, sb, (int)M, (int)N, (int)K, c, ctype);
+  k_gemm<kWaves><<<dim3((unsigned)tiles), dim3(64 * kWaves), 0, st>>>(a, sa, b, sb, (int)M, (int)N, (int)K, c, ctype);
   return hipGetLastError();
 }
 
