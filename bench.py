@@ -13,6 +13,8 @@ inside the timed loop, and the CPU oracle timed on a bounded sample of the same 
 
 Other workloads (--workload) time one kernel each against the HBM roofline, rotating
 through >= 1 GiB of buffer sets so the 256 MB Infinity Cache cannot serve them.
+`--workload hbm_copy` times a plain 1 GiB device-to-device copy: the reference point
+that scales the HBM byte counters of the kernels above.
 """
 import argparse
 import json
@@ -169,35 +171,77 @@ def _rotating(make, nbytes_per_set, min_total=1 << 30):
     return [make() for _ in range(sets)]
 
 
-def run_memory_workload(args):
-    name = args.workload
+def run_hbm_copy(args):
+    """A plain copy of 1 GiB (read 1 GiB, write 1 GiB) with torch's copy kernel."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t = Timer()
+    for _ in range(args.steps):
+        s = t.start()
+        dst.copy_(src)
+        t.stop(s)
+    torch.cuda.synchronize()
+    kms = t.mean_ms()
+    gbs = 2 * n / (kms * 1e-3) / 1e9
+    return {"metric": "device-to-device copy GB/s (read + write)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": kms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "hbm_copy: 1 GiB device-to-device copy (counter calibration)"},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "torch copy",
+                         "kernel_ms": kms, "bytes_per_launch": 2 * n}}
+
+
+def _memory_case(name, op):
+    """(make, launch, bytes per launch, kernel label) of one memory-bound workload op."""
     wl = W.WORKLOADS[name]
+    M, K = wl.shape
     if name == "mxfp4_h32":
         x_cpu = W.mxfp4_h32_input(wl.shape, wl.seed)
-        M, K = wl.shape
         nbytes = M * K * 2 + M * K // 2 + M * K // 32
+        if op == "quant":
+            def make():
+                return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
+                        torch.empty((M, K // 32), dtype=torch.uint8, device=DEV))
+
+            def launch(s):
+                fp4.fp4_quantize(s[0], "mxfp4", 32, codes=s[1], scales=s[2])
+            return make, launch, nbytes, "k_quant_mx<bf16,32>"
+        codes, scales, _ = fp4.fp4_quantize(x_cpu.to(DEV), "mxfp4", 32)
 
         def make():
-            return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
-                    torch.empty((M, K // 32), dtype=torch.uint8, device=DEV))
+            return (codes.clone(), scales.clone(), torch.empty((M, K), dtype=torch.bfloat16, device=DEV))
 
         def launch(s):
-            fp4.fp4_quantize(s[0], "mxfp4", 32, codes=s[1], scales=s[2])
-        kernel = "k_quant_mx<bf16,32>"
-    elif name == "dualscale_pack":
+            fp4.fp4_dequantize(s[0], s[1], None, "mxfp4", 32, y=s[2])
+        return make, launch, nbytes, "k_dequant<MX,32,bf16> (inverse H32)"
+    if name == "dualscale_pack":
         x_cpu = W.student_t_input(wl.shape, wl.seed)
-        M, K = wl.shape
         nbytes = M * K * 2 + M * K // 2 + M * K // 16 + 4 * M * K // 128
+        nb = fp4.fp4_pack_bytes(M, K)
+        if op == "quant":
+            def make():
+                return (x_cpu.to(DEV), torch.empty(nb, dtype=torch.uint8, device=DEV))
+
+            def launch(s):
+                fp4.fp4_pack(s[0], packed=s[1])
+            return make, launch, nbytes, "k_pack"
+        packed = fp4.fp4_pack(x_cpu.to(DEV))
 
         def make():
-            return (x_cpu.to(DEV), torch.empty(fp4.fp4_pack_bytes(M, K), dtype=torch.uint8, device=DEV))
+            return (packed.clone(), torch.empty((M, K), dtype=torch.bfloat16, device=DEV))
 
         def launch(s):
-            fp4.fp4_pack(s[0], packed=s[1])
-        kernel = "k_pack"
-    elif name == "arcquant":
+            fp4.fp4_unpack(s[0], M, K, y=s[1])
+        return make, launch, nbytes, "k_unpack"
+    if name == "arcquant":
+        if op != "quant":
+            raise SystemExit("arcquant has no inverse op")
         x_cpu = W.arcquant_input(wl.shape, wl.seed)
-        M, K = wl.shape
         S = wl.extra["S"]
         perm = torch.from_numpy(W.calibration_order(x_cpu)).to(DEV)
         ts = torch.zeros(1, dtype=torch.float32, device=DEV)
@@ -210,43 +254,62 @@ def run_memory_workload(args):
 
         def launch(s):
             fp4.fp4_residual_quantize(s[0], perm, S, codes=s[1], scales=s[2], tensor_scale=ts, mode="given")
-        kernel = "k_arcquant<false> (static tensor scale)"
-    elif name == "nvfp4_roundtrip":
+        return make, launch, nbytes, "k_arcquant<false> (static tensor scale)"
+    if name == "nvfp4_roundtrip":
+        if op != "quant":
+            raise SystemExit("nvfp4_roundtrip times quantize + dequantize together")
         x_cpu = W.nvfp4_roundtrip_input(wl.shape, wl.seed)
-        M, K = wl.shape
-        nbytes = M * K * 4 + M * K // 2 + M * K // 16 + 4
+        nbytes = 2 * (M * K * 4 + M * K // 2 + M * K // 16 + 4)
 
         def make():
             return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
                     torch.empty((M, K // 16), dtype=torch.uint8, device=DEV),
-                    torch.zeros(1, dtype=torch.float32, device=DEV))
+                    torch.zeros(1, dtype=torch.float32, device=DEV),
+                    torch.empty((M, K), dtype=torch.float32, device=DEV))
 
         def launch(s):
             fp4.fp4_quantize(s[0], "nvfp4", 0, codes=s[1], scales=s[2], tensor_scale=s[3])
-        kernel = "NVFP4 exact quantize (amax pass + quant)"
-    else:
-        raise SystemExit(f"unknown workload {name}")
+            fp4.fp4_dequantize(s[1], s[2], s[3], "nvfp4", 0, y=s[4])
+        return make, launch, nbytes, "NVFP4 round trip (amax, quantize, dequantize kernels)"
+    raise SystemExit(f"unknown workload {name}")
+
+
+def run_memory_workload(args):
+    """K launches over rotating buffer sets, captured once into a HIP graph so that the
+    host's launch cost does not pace these short kernels; the timed region is one replay
+    bracketed by one HIP event pair on the replay stream."""
+    name, op = args.workload, args.op
+    wl = W.WORKLOADS[name]
+    make, launch, nbytes, kernel = _memory_case(name, op)
     sets = _rotating(make, nbytes)
     for i in range(args.warmup):
         launch(sets[i % len(sets)])
     torch.cuda.synchronize()
-    t = Timer()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(args.steps):
+            launch(sets[i % len(sets)])
+    g.replay()                                   # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        s = t.start()
-        launch(sets[i % len(sets)])
-        t.stop(s)
+    e0.record()
+    g.replay()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kms = t.mean_ms()
+    kms = e0.elapsed_time(e1) / args.steps
     gbs = nbytes / (kms * 1e-3) / 1e9
-    out = {"metric": METRIC, "value": nbytes / (wall / args.steps) / 1e9, "unit": "GB/s", "n_gpus": 1,
+    out = {"metric": METRIC, "value": nbytes * args.steps / wall / 1e9, "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp4 out",
-           "data": "synthetic", "config": {"workload": f"{name}: {wl.description}"},
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp32 arithmetic; bf16/fp32 in, e2m1 + e4m3/e8m0 out" if op == "quant"
+           else "fp32 arithmetic; e2m1 + e4m3/e8m0 in, bf16/fp32 out",
+           "data": "synthetic", "config": {"workload": f"{name} ({op}): {wl.description}"},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(name), "kernel": kernel,
-                        "kernel_ms": kms, "bytes_per_launch": nbytes, "buffer_sets": len(sets)}}
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(f"{name}_{op}"), "kernel": kernel,
+                        "kernel_ms": kms, "bytes_per_launch": nbytes, "buffer_sets": len(sets),
+                        "timing": "one HIP event pair around a graph replay of `steps` launches"}}
     return out
 
 
@@ -255,7 +318,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="w4a4_gemm", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="w4a4_gemm", choices=sorted(W.WORKLOADS) + ["hbm_copy"])
+    ap.add_argument("--op", default="quant", choices=["quant", "dequant"],
+                    help="memory workloads: time the forward op (quantize / pack) or its inverse")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -265,7 +330,12 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     fp4.lib()                                   # fail loudly if the HIP library is missing
-    out = run_w4a4_gemm(args) if args.workload == "w4a4_gemm" else run_memory_workload(args)
+    if args.workload == "w4a4_gemm":
+        out = run_w4a4_gemm(args)
+    elif args.workload == "hbm_copy":
+        out = run_hbm_copy(args)
+    else:
+        out = run_memory_workload(args)
     print(json.dumps(out), flush=True)
 
 
