@@ -8,14 +8,21 @@
 // kernel for reorder, RMSNorm, primary and residual quantization emitting the GEMM-ready
 // layout (item 5).
 //
-// One workgroup walks rows (persistent, stride gridDim.x).  Per row: coalesced 16-element
-// loads accumulate sum(x^2) and park x as fp32 in LDS; a workgroup reduction gives
-// 1/rms; each lane then gathers its 16 reordered channels z[c] = x[perm[c]] / rms * gamma
-// from LDS (perm is staged in LDS once per workgroup) and encodes them; lanes whose block
-// lies in the first S channels also encode the residual z - V s_b s_t (one fma, a single
-// rounding of the exact difference).  The dynamic tensor scale needs max|z| first: the
-// same kernel runs once in statistics mode (identical arithmetic up to z) before the
-// quantizing launch.
+// Work decomposition (gfx950): one wave owns one row at a time, so the row reduction is a
+// wave reduction and no workgroup barrier sits on the per-row path.
+//   1. The row streams in with coalesced 16-byte loads (eight per lane in flight), its
+//      sum of squares accumulates in registers, and the raw bf16 row is parked in the
+//      wave's own LDS slice.
+//   2. A butterfly sum gives every lane the same sum, hence the same 1/rms.
+//   3. Lane l then encodes blocks l, l + 64, ...: the 16 channel indices of a block come
+//      from the permutation, staged once per workgroup in LDS as 16-bit indices, and the
+//      16 values are gathered from the LDS row.  Codes leave as 8-byte stores (512
+//      contiguous bytes per wave instruction), block scales as bytes (64 contiguous).
+//      Lanes whose block lies in the first S channels also encode the residual
+//      z - V s_b s_t (one fma: a single rounding of the exact difference).
+// The dynamic tensor scale needs max|z| over the tensor first.  The maximum does not
+// depend on channel order, so the statistics pass streams rows without the gather, with
+// the same per-element arithmetic as the quantizing pass.
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
 
@@ -23,89 +30,232 @@ using namespace fp4dev;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kMaxWaves = 8;
+constexpr int kLdsLimit = 144 * 1024;       // dynamic LDS per workgroup used here
+constexpr int kUnroll = 8;          // 16-byte loads in flight per lane
+#ifndef ARC_PIPE_WAVES
+#define ARC_PIPE_WAVES 8
+#endif
+#ifndef ARC_PIPE_TOTAL
+#define ARC_PIPE_TOTAL 4096
+#endif
+// Rows of at most 64 kUnroll 16-byte units are software-pipelined: kPipeWaves waves per
+// workgroup and at most kPipeTotal waves in all (16 per CU), each walking several
+// rows with the next row's loads in flight.
+constexpr int kPipeWaves = ARC_PIPE_WAVES;
+constexpr int kPipeTotal = ARC_PIPE_TOTAL;
 
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 __global__ void k_finalize_tensor_scale(float* p) { *p = *p / 2688.0f; }
 
-template <bool STATS>
-__global__ void __launch_bounds__(kThreads)
-k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
-           const int32_t* __restrict__ perm, int S, uint8_t* __restrict__ codes,
-           uint8_t* __restrict__ scales, float* tensor_scale, float* __restrict__ dbg) {
-  extern __shared__ float smem[];
-  float* xs = smem;                                        // [K] row values
-  int32_t* ps = reinterpret_cast<int32_t*>(smem + K);      // [K] permutation
-  __shared__ float red[kWaves];
+// Make this wave's LDS writes visible to its own later LDS reads (and the reverse).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
 
-  const int t = threadIdx.x;
-  const int nblk = K / 16;
-  // an index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced
-  for (int c = t; c < K; c += kThreads) ps[c] = (int32_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
-  const float s_t = STATS ? 0.0f : *tensor_scale;
-  const int64_t row_codes = (K + S) / 2, row_scales = (K + S) / 16;
-  float tmax = 0.0f;
+// One chunk of a row: kUnroll 16-byte units per lane (unit u0 + 64 i + lane), zero past
+// the end.
+__device__ __forceinline__ void load_units(const uint16_t* __restrict__ xr, int u0, int units, int lane,
+                                           uint4 (&raw)[kUnroll]) {
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const int u = u0 + 64 * i + lane;
+    raw[i] = u < units ? reinterpret_cast<const uint4*>(xr)[u] : make_uint4(0, 0, 0, 0);
+  }
+}
 
-  for (int64_t r = blockIdx.x; r < M; r += gridDim.x) {
-    const uint16_t* xr = x + r * K;
-    float ss = 0.0f;
-    for (int b = t; b < nblk; b += kThreads) {
-      float v[16];
-      load_bf16<16>(xr + 16 * b, v);
+// Lane-local sum of squares of one chunk (fixed order) and its copy into the LDS row.
+__device__ __forceinline__ float park_units(const uint4 (&raw)[kUnroll], int u0, int units, int lane,
+                                            uint16_t* xs, float ss) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(v[i], v[i], ss);
+  for (int i = 0; i < kUnroll; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<float4*>(xs + 16 * b + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    for (int k = 0; k < 4; ++k) {
+      const float a = bf16_lo(w[k]), b = bf16_hi(w[k]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
     }
-    ss = wave_sum(ss);
-    if ((t & 63) == 0) red[t >> 6] = ss;
-    __syncthreads();                                       // xs, ps and red complete
-    float tot = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += red[w];
-    const float inv_rms = 1.0f / sqrtf(tot / (float)K + eps);
+    const int u = u0 + 64 * i + lane;
+    if (u < units) reinterpret_cast<uint4*>(xs)[u] = raw[i];
+  }
+  return ss;
+}
 
-    for (int b = t; b < nblk; b += kThreads) {
+// Stream one row: sum of squares in a fixed order (lane-local over its units, then a
+// butterfly), raw bf16 parked at xs.  Identical arithmetic in every pass.
+__device__ __forceinline__ float load_row(const uint16_t* __restrict__ xr, int units, int lane, uint16_t* xs) {
+  float ss = 0.0f;
+  for (int u0 = 0; u0 < units; u0 += 64 * kUnroll) {
+    uint4 raw[kUnroll];
+    load_units(xr, u0, units, lane, raw);
+    ss = park_units(raw, u0, units, lane, xs, ss);
+  }
+  return wave_sum(ss);
+}
+
+__device__ __forceinline__ float inv_rms_of(float ss, int K, float eps) {
+  return 1.0f / sqrtf(ss / (float)K + eps);
+}
+
+// z = fl(x / rms) (times gamma[c] when given): the normalised value of channel c.
+__device__ __forceinline__ float norm_value(uint16_t xb, float inv_rms, const float* __restrict__ gamma, int c) {
+  const float y = __uint_as_float((uint32_t)xb << 16) * inv_rms;
+  return gamma ? y * gamma[c] : y;
+}
+
+// Statistics pass: running max|z| over the rows this wave visits, one atomic per wave.
+__global__ void __launch_bounds__(64 * kMaxWaves)
+k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
+            float* tensor_scale) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint16_t* xs = smem + (size_t)wave * K;
+  const int units = K / 8;
+  float tmax = 0.0f;
+  for (int64_t r = (int64_t)blockIdx.x * W + wave; r < M; r += (int64_t)gridDim.x * W) {
+    const float ss = load_row(x + r * K, units, lane, xs);
+    const float inv_rms = inv_rms_of(ss, K, eps);
+    wave_lds_sync();
+    for (int u = lane; u < units; u += 64) {
+      const uint4 w = reinterpret_cast<const uint4*>(xs)[u];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        tmax = fmaxf(tmax, fabsf(norm_value((uint16_t)ws[k], inv_rms, gamma, 8 * u + 2 * k)));
+        tmax = fmaxf(tmax, fabsf(norm_value((uint16_t)(ws[k] >> 16), inv_rms, gamma, 8 * u + 2 * k + 1)));
+      }
+    }
+    wave_lds_sync();
+  }
+  tmax = wave_max(tmax);
+  if (lane == 0 && tmax > 0.0f) atomic_max_nonneg(tensor_scale, tmax);
+}
+
+// Encode one 16-channel block: primary NVFP4 codes and scale, and for blocks inside the
+// first S channels the residual z - V s_b s_t and its codes and scale.
+__device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K, int nblk, int sblk, float s_t,
+                                             uint8_t* __restrict__ crow, uint8_t* __restrict__ srow) {
+  const uint32_t sb = nvfp4_block_scale(absmax<16>(z), s_t);
+  const float sbv = e4m3_value(sb);
+  const float S32 = sbv * s_t;
+  const float E = S32 > 0.0f ? 1.0f / S32 : 0.0f;
+  const uint2 w = nvfp4_encode16_fast(z, E);
+  *reinterpret_cast<uint2*>(crow + 8 * b) = w;
+  srow[b] = (uint8_t)sb;
+  if (b < sblk) {
+    float q[16];
+    e2m1_decode8(w.x, 1.0f, q);
+    e2m1_decode8(w.y, 1.0f, q + 8);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, z[i]);   // z - V s_b s_t
+    const uint32_t sr = nvfp4_block_scale(absmax<16>(q), s_t);
+    const float R32 = e4m3_value(sr) * s_t;
+    const float Er = R32 > 0.0f ? 1.0f / R32 : 0.0f;
+    *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, Er);
+    srow[nblk + b] = (uint8_t)sr;
+  }
+}
+
+// Gather, normalise and encode row r from its LDS copy: lane l takes blocks l + 64 j.
+// kBlocks blocks per lane are gathered together (all their LDS reads in flight at once)
+// before any of them is encoded.
+constexpr int kBlocks = 1;
+__device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
+                                           int lane, float inv_rms, const float* __restrict__ gamma, float s_t,
+                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                           float* __restrict__ dbg) {
+  const int nblk = K / 16, sblk = S / 16;
+  const int64_t row_codes = (K + S) / 2, row_scales = (K + S) / 16;
+  uint8_t* crow = codes + r * row_codes;
+  uint8_t* srow = scales + r * row_scales;
+  for (int b0 = lane; b0 < nblk; b0 += 64 * kBlocks) {
+    uint4 pw[kBlocks][2];
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) {
+      const int b = min(b0 + 64 * j, nblk - 1);            // past the end: a valid dummy block
+      pw[j][0] = reinterpret_cast<const uint4*>(ps)[2 * b];
+      pw[j][1] = reinterpret_cast<const uint4*>(ps)[2 * b + 1];
+    }
+    uint16_t xv[kBlocks][16];
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) {
+      const uint32_t w[8] = {pw[j][0].x, pw[j][0].y, pw[j][0].z, pw[j][0].w,
+                             pw[j][1].x, pw[j][1].y, pw[j][1].z, pw[j][1].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xv[j][2 * k] = xs[w[k] & 0xFFFFu];
+        xv[j][2 * k + 1] = xs[w[k] >> 16];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) {
+      const int b = b0 + 64 * j;
+      if (b >= nblk) break;
+      const uint32_t w[8] = {pw[j][0].x, pw[j][0].y, pw[j][0].z, pw[j][0].w,
+                             pw[j][1].x, pw[j][1].y, pw[j][1].z, pw[j][1].w};
       float z[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        int p = ps[16 * b + i];
-        float y = xs[p] * inv_rms;
-        z[i] = gamma ? y * gamma[p] : y;
+      for (int k = 0; k < 8; ++k) {
+        z[2 * k] = norm_value(xv[j][2 * k], inv_rms, gamma, (int)(w[k] & 0xFFFFu));
+        z[2 * k + 1] = norm_value(xv[j][2 * k + 1], inv_rms, gamma, (int)(w[k] >> 16));
       }
       if (dbg) store_f32<16>(dbg + r * K + 16 * b, z);
-      if constexpr (STATS) {
-        tmax = fmaxf(tmax, absmax<16>(z));
-      } else {
-        uint32_t sb = nvfp4_block_scale(absmax<16>(z), s_t);
-        float sbv = e4m3_value(sb);
-        float S32 = sbv * s_t;
-        float E = S32 > 0.0f ? 1.0f / S32 : 0.0f;
-        uint2 w = nvfp4_encode16_fast(z, E);
-        *reinterpret_cast<uint2*>(codes + r * row_codes + 8 * b) = w;
-        scales[r * row_scales + b] = (uint8_t)sb;
-        if (16 * b < S) {
-          float q[16];
-          e2m1_decode8(w.x, 1.0f, q);
-          e2m1_decode8(w.y, 1.0f, q + 8);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, z[i]);   // z - V s_b s_t
-          uint32_t sr = nvfp4_block_scale(absmax<16>(q), s_t);
-          float R32 = e4m3_value(sr) * s_t;
-          float Er = R32 > 0.0f ? 1.0f / R32 : 0.0f;
-          *reinterpret_cast<uint2*>(codes + r * row_codes + K / 2 + 8 * b) = nvfp4_encode16_fast(q, Er);
-          scales[r * row_scales + nblk + b] = (uint8_t)sr;
-        }
-      }
+      encode_block(z, b, K, nblk, sblk, s_t, crow, srow);
     }
-    __syncthreads();                                       // xs reused by the next row
   }
-  if constexpr (STATS) {
-    tmax = wave_max(tmax);
-    if ((t & 63) == 0 && tmax > 0.0f) atomic_max_nonneg(tensor_scale, tmax);
+}
+
+__global__ void __launch_bounds__(64 * kMaxWaves)
+k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
+           const int32_t* __restrict__ perm, int S, uint8_t* __restrict__ codes,
+           uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, float* __restrict__ dbg) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint16_t* ps = smem;                                   // [K] permutation (16-bit)
+  uint16_t* xs = smem + (size_t)(1 + wave) * K;          // [K] this wave's row
+
+  // an index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced
+  for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
+  __syncthreads();
+
+  const float s_t = *tensor_scale;
+  const int units = K / 8;
+  const int64_t stride = (int64_t)gridDim.x * W;
+  int64_t r = (int64_t)blockIdx.x * W + wave;
+  if (units <= 64 * kUnroll) {
+    // whole row in one chunk: the next row's loads are in flight while this row is encoded
+    uint4 raw[kUnroll];
+    if (r < M) load_units(x + r * K, 0, units, lane, raw);
+    for (; r < M; r += stride) {
+      const float ss = wave_sum(park_units(raw, 0, units, lane, xs, 0.0f));
+      if (r + stride < M) load_units(x + (r + stride) * K, 0, units, lane, raw);
+      wave_lds_sync();
+      encode_row(xs, ps, r, K, S, lane, inv_rms_of(ss, K, eps), gamma, s_t, codes, scales, dbg);
+      wave_lds_sync();                                   // xs is refilled by the next row
+    }
+  } else {
+    for (; r < M; r += stride) {
+      const float ss = load_row(x + r * K, units, lane, xs);
+      wave_lds_sync();
+      encode_row(xs, ps, r, K, S, lane, inv_rms_of(ss, K, eps), gamma, s_t, codes, scales, dbg);
+      wave_lds_sync();
+    }
   }
+}
+
+// Waves per workgroup: one LDS row each plus the shared permutation, within 144 KiB.
+int waves_for(int64_t K) {
+  int64_t w = kLdsLimit / (2 * K) - 1;
+  return (int)(w > kMaxWaves ? kMaxWaves : (w < 1 ? 1 : w));
+}
+
+hipError_t allow_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace
@@ -116,24 +266,23 @@ hipError_t launch_residual_quantize(const uint16_t* x, int64_t M, int64_t K, con
                                     float eps, const int32_t* perm, int64_t S, uint8_t* codes,
                                     uint8_t* scales, float* ts, bool compute, float* dbg,
                                     hipStream_t st) {
-  size_t lds = (size_t)K * 8;
-  if (lds > 65536) {   // rows beyond 8192 channels need more than the default 64 KiB of LDS
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_arcquant<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_arcquant<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  unsigned grid = (unsigned)(M < 2048 ? (M > 0 ? M : 1) : 2048);
+  const int W = waves_for(K);
+  const int64_t rows_per_grid = 1024 * (int64_t)W;       // at most 1024 workgroups, persistent beyond
+  const unsigned grid = (unsigned)(M <= 0 ? 1 : (M < rows_per_grid ? (M + W - 1) / W : 1024));
+  const bool pipelined = K / 8 <= 64 * kUnroll;
+  const int Wq = pipelined ? kPipeWaves : W;
+  const int64_t wq_total = pipelined ? (M < kPipeTotal ? M : kPipeTotal) : (M < rows_per_grid ? M : rows_per_grid);
+  const unsigned grid_q = (unsigned)(wq_total <= 0 ? 1 : (wq_total + Wq - 1) / Wq);
+  const size_t lds_stats = (size_t)2 * K * W, lds_quant = (size_t)2 * K * (Wq + 1);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arc_stats), lds_stats);
+  if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(k_arcquant), lds_quant);
+  if (e != hipSuccess) return e;
   if (compute) {
     k_zero_scalar<<<1, 1, 0, st>>>(ts);
-    if (M) k_arcquant<true><<<grid, kThreads, lds, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes,
-                                                        scales, ts, nullptr);
+    if (M) k_arc_stats<<<grid, 64 * W, lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
     k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
-  if (M) k_arcquant<false><<<grid, kThreads, lds, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes,
-                                                       scales, ts, dbg);
+  if (M) k_arcquant<<<grid_q, 64 * Wq, lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes, scales, ts, dbg);
   return hipGetLastError();
 }
 

@@ -84,3 +84,18 @@ def test_arcquant_config_full_size():
     rows = W.seeded_rows(4096, 64, 40)
     n = _check_arc(xt, perm, 256, rows=rows)
     print(f"  boundary-tolerated code differences: {n}", flush=True)
+
+
+@pytest.mark.parametrize("M,K,S,gam", [(9000, 256, 64, False), (40, 8192, 512, False), (37, 12288, 256, True)])
+def test_arcquant_multi_row_and_long_rows(M, K, S, gam):
+    """More rows than resident waves (each wave walks several rows, prefetching the next)
+    and rows longer than one 4096-channel chunk (the row streams in several chunks)."""
+    print(f"arcquant M={M} K={K} S={S} gamma={gam}", flush=True)
+    rng = np.random.default_rng(M + K + S)
+    x = rng.standard_normal((M, K))
+    x[:, rng.choice(K, max(1, K // 64), replace=False)] *= 30
+    xt = W.to_bf16(x)
+    perm = W.calibration_order(xt)
+    gamma = rng.uniform(0.5, 1.5, K) if gam else None
+    rows = np.unique(np.concatenate([W.seeded_rows(M, min(M, 48), 9), [0, M - 1]]))
+    _check_arc(xt, perm, S, gamma=gamma, rows=rows)
