@@ -72,7 +72,7 @@ class Timer:
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline_gemm(a_bf16, w_bf16, rows=4096, cols=8192):
+def cpu_baseline_gemm(a_bf16, w_bf16, rows=8192, cols=16384):
     """Oracle (float64 numpy) on a bounded sample of the step: Hadamard-32 MXFP4 of `rows`
     activation rows, then their GEMM against `cols` weight rows quantized the same way
     (untimed setup).  Throughput in the step's unit: 2 rows cols K / time."""

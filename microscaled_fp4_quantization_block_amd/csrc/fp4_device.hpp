@@ -23,8 +23,11 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Two values to a packed bf16 pair, nearest-even (gfx950 v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+  const bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Load N consecutive elements (N % 8 == 0) as fp32 with 16-byte loads.
@@ -258,6 +261,83 @@ __device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
 // 2^(code - 127) as a binary32 (code 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_value(uint32_t code) {
   return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+}
+
+// --------------------------------------------------------------------------- DPP quads
+
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]: value of lane ^ 1
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]: value of lane ^ 2
+constexpr int kQuadRev = 0x1B;    // quad_perm [3,2,1,0]: value of lane ^ 3
+constexpr int kRowHalfMirror = 0x141;   // value of lane ^ 7 within 8 lanes
+constexpr int kRowMirror = 0x140;       // value of lane ^ 15 within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Value held by lane ^ X (X = 1, 2, 4 or 8; 4 and 8 compose two row permutations).
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (X == 1) return dpp_move<kQuadXor1>(v);
+  else if constexpr (X == 2) return dpp_move<kQuadXor2>(v);
+  else if constexpr (X == 4) return dpp_move<kQuadRev>(dpp_move<kRowHalfMirror>(v));   // (i ^ 7) ^ 3
+  else return dpp_move<kRowHalfMirror>(dpp_move<kRowMirror>(v));                     // (i ^ 15) ^ 7
+}
+
+template <int CTRL>
+__device__ __forceinline__ float quad_partner(float v) {
+  return dpp_move<CTRL>(v);
+}
+
+// One Walsh-Hadamard butterfly across lane pairs: the lower lane (bit clear) keeps
+// own + partner, the upper one partner - own, i.e. (a + b, a - b) exactly as the in-lane
+// butterfly computes them (fma with -1 is an exact negation inside one rounding).
+template <int X>
+__device__ __forceinline__ float lane_butterfly(float own, float sign) {
+  return fmaf(own, sign, lane_xor<X>(own));
+}
+
+// Orthonormal H_B over a block spread as 8 contiguous elements per lane across B / 8
+// consecutive lanes of a quad (lane p = position within the quad): the in-lane stages
+// first (index bits 0-2), then the lane bits, then the 1/sqrt(B) scaling -- the same
+// stage order, hence the same roundings, as block_hadamard on the whole block.
+template <int B>
+__device__ __forceinline__ void quad_hadamard8(float (&v)[8], int p) {
+  if constexpr (B >= 16) {
+    fwht_inplace<8>(v);
+    const float s1 = (p & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<1>(v[j], s1);
+    if constexpr (B == 32) {
+      const float s2 = (p & 2) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<2>(v[j], s2);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= InvSqrt<B>::v;
+  }
+}
+
+// Two-level FWHT of a 128-group spread as 8 contiguous elements per lane over 16
+// consecutive lanes (lane g of the group holds elements 8 g .. 8 g + 7): level 1 is H_16
+// inside each micro-group (in-lane bits, then lane bit 0), level 2 is H_8 across the
+// micro-groups (lane bits 1-3); normalised once at the end.  Same stage order as
+// two_level_fwht128 on the whole group.
+__device__ __forceinline__ void group16_two_level_fwht8(float (&v)[8], int g) {
+  fwht_inplace<8>(v);
+  const float s1 = (g & 1) ? -1.0f : 1.0f, s2 = (g & 2) ? -1.0f : 1.0f;
+  const float s4 = (g & 4) ? -1.0f : 1.0f, s8 = (g & 8) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<1>(v[j], s1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<2>(v[j], s2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<4>(v[j], s4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<8>(v[j], s8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] *= InvSqrt<128>::v;
 }
 
 // --------------------------------------------------------------------------- reductions

@@ -1,9 +1,9 @@
 // FP4Quant-style micro-grouped dual-scale FP4 pack / unpack with the two-level FWHT.
 //
 // Source: FP4Quant abstract (paperdot.bitmofang.com): a hybrid two-level FWHT ahead of a
-// micro-grouped dual-scale FP4 quantization, and a cooperative sub-byte packing.  Here a
-// 128-group is spread over the four lanes of a DPP quad, each lane owning 32 contiguous
-// elements (two 16-element micro-groups, one 16-byte code store):
+// micro-grouped dual-scale FP4 quantization, and a cooperative sub-byte packing.  In the
+// pack a 128-group is spread over the four lanes of a DPP quad, each lane owning 32
+// contiguous elements (two 16-element micro-groups, one 16-byte code store):
 //   level 1   H_16 inside each micro-group: in-lane butterflies;
 //   level 2   H_8 across the 8 micro-groups (index 2 p + h for lane p of the quad and
 //             micro-group h of the lane): the h butterfly is in-lane, the two lane-bit
@@ -20,14 +20,6 @@ using namespace fp4dev;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
-
-template <int CTRL>
-__device__ __forceinline__ float quad_partner(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
 template <int CTRL>
 __device__ __forceinline__ float quad_max(float m) {
   return fmaxf(m, quad_partner<CTRL>(m));
@@ -81,26 +73,36 @@ k_pack(const uint16_t* x, int64_t nchunks, uint8_t* codes, uint8_t* micro, float
   if (p == 0) group[c >> 2] = s_g;
 }
 
+// Unpack by groups of 16 lanes: lane g of a group owns elements 8 g .. 8 g + 7 of one
+// 128-group (one 4-byte code word), so a wave's bf16 stores are 1 KiB contiguous; the
+// two-level FWHT finishes with DPP butterflies across the 16 lanes.
+constexpr int kUnpackUnits = 2;
+
 __global__ void __launch_bounds__(kThreads)
-k_unpack(const uint8_t* codes, const uint8_t* micro, const float* group, int64_t nchunks, uint16_t* y) {
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= nchunks) return;
-  const int p = (int)(c & 3);
-  uint4 w = reinterpret_cast<const uint4*>(codes)[c];
-  uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  uint32_t sm2 = reinterpret_cast<const uint16_t*>(micro)[c];
-  const float s_g = group[c >> 2];
-  float v[32];
+k_unpack(const uint8_t* codes, const uint8_t* micro, const float* group, int64_t n8, uint16_t* y) {
+  const int64_t base = (int64_t)blockIdx.x * (kUnpackUnits * kThreads) + threadIdx.x;
+  const int g = threadIdx.x & 15;
+  uint32_t cw[kUnpackUnits], sm[kUnpackUnits];
+  float sg[kUnpackUnits];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) e2m1_decode8(ws[i], 1.0f, v + 8 * i);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float sm = e4m3_value((sm2 >> (8 * h)) & 0xFFu);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[16 * h + i] = (v[16 * h + i] * sm) * s_g;   // V s_m exact
+  for (int u = 0; u < kUnpackUnits; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    const bool ok = i < n8;
+    cw[u] = ok ? reinterpret_cast<const uint32_t*>(codes)[i] : 0u;
+    sm[u] = ok ? (uint32_t)micro[i >> 1] : 0u;
+    sg[u] = ok ? group[i >> 4] : 0.0f;
   }
-  quad_two_level_fwht(v, p);
-  store_bf16<32>(y + c * 32, v);
+#pragma unroll
+  for (int u = 0; u < kUnpackUnits; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    float v[8];
+    e2m1_decode8(cw[u], 1.0f, v);
+    const float smv = e4m3_value(sm[u]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (v[j] * smv) * sg[u];     // V s_m exact
+    group16_two_level_fwht8(v, g);                               // every lane takes part
+    if (i < n8) store_bf16<8>(y + i * 8, v);
+  }
 }
 
 }  // namespace
@@ -128,11 +130,11 @@ hipError_t launch_pack(const uint16_t* x, int64_t M, int64_t K, uint8_t* packed,
 }
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t M, int64_t K, uint16_t* y, hipStream_t st) {
-  int64_t n = M * K / 32;
-  if (!n) return hipSuccess;
+  const int64_t n8 = M * K / 8, per_block = (int64_t)kUnpackUnits * kThreads;
+  if (!n8) return hipSuccess;
   PackLayout L = pack_layout(M, K);
-  k_unpack<<<dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, st>>>(
-      packed, packed + L.off_micro, reinterpret_cast<const float*>(packed + L.off_group), n, y);
+  k_unpack<<<dim3((unsigned)((n8 + per_block - 1) / per_block)), dim3(kThreads), 0, st>>>(
+      packed, packed + L.off_micro, reinterpret_cast<const float*>(packed + L.off_group), n8, y);
   return hipGetLastError();
 }
 

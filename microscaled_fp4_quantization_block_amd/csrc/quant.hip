@@ -95,36 +95,46 @@ k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
 }
 
 // Dequantization: fl32(V s_b s_t) (NVFP4) or V 2^(e-127) (MXFP4), optional H, store.
+// Written by quads: lane p of a quad owns elements 8 p .. 8 p + 7 of a 32-element chunk
+// (one 4-byte code word), so the stores of a wave are 1 KiB contiguous for bf16 output;
+// rotation finishes with DPP butterflies across the quad.  kDeqUnits units per lane,
+// all loads issued before any conversion.
+constexpr int kDeqUnits = 4;
+
 template <int FMT, int H, int OUT>
 __global__ void __launch_bounds__(kThreads)
-k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t nchunks,
-          void* y) {
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= nchunks) return;
-  uint4 w = reinterpret_cast<const uint4*>(codes)[c];
-  uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float v[32];
-  if constexpr (FMT == fp4impl::FMT_MX) {
-    float sc = e8m0_value(scales[c]);
+k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t n8, void* y) {
+  const int64_t base = (int64_t)blockIdx.x * (kDeqUnits * kThreads) + threadIdx.x;
+  const int p = threadIdx.x & 3;
+  uint32_t cw[kDeqUnits], sc[kDeqUnits];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e2m1_decode8(ws[i], sc, v + 8 * i);
-  } else {
-    const float s_t = *tensor_scale;
-    uint32_t sb2 = reinterpret_cast<const uint16_t*>(scales)[c];
+  for (int u = 0; u < kDeqUnits; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    const bool ok = i < n8;
+    cw[u] = ok ? reinterpret_cast<const uint32_t*>(codes)[i] : 0u;
+    sc[u] = ok ? (uint32_t)scales[FMT == fp4impl::FMT_MX ? (i >> 2) : (i >> 1)] : 0u;
+  }
+  const float s_t = FMT == fp4impl::FMT_MX ? 0.0f : *tensor_scale;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e2m1_decode8(ws[i], 1.0f, v + 8 * i);
+  for (int u = 0; u < kDeqUnits; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    float v[8];
+    if constexpr (FMT == fp4impl::FMT_MX) {
+      e2m1_decode8(cw[u], e8m0_value(sc[u]), v);
+    } else {
+      e2m1_decode8(cw[u], 1.0f, v);
+      const float sb = e4m3_value(sc[u]);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float sb = e4m3_value((sb2 >> (8 * b)) & 0xFFu);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[16 * b + i] = (v[16 * b + i] * sb) * s_t;   // V s_b exact
+      for (int j = 0; j < 8; ++j) v[j] = (v[j] * sb) * s_t;     // V s_b exact
+    }
+    quad_hadamard8<H>(v, p);                                    // every lane takes part
+    if (i < n8) {
+      if constexpr (OUT == fp4impl::DT_F32)
+        store_f32<8>(reinterpret_cast<float*>(y) + i * 8, v);
+      else
+        store_bf16<8>(reinterpret_cast<uint16_t*>(y) + i * 8, v);
     }
   }
-  block_hadamard<32, H>(v);
-  if constexpr (OUT == fp4impl::DT_F32)
-    store_f32<32>(reinterpret_cast<float*>(y) + c * 32, v);
-  else
-    store_bf16<32>(reinterpret_cast<uint16_t*>(y) + c * 32, v);
 }
 
 inline dim3 grid_for(int64_t nchunks) { return dim3((unsigned)((nchunks + kThreads - 1) / kThreads)); }
@@ -150,11 +160,12 @@ template <int FMT, int H>
 hipError_t dequant_t(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t nchunks,
                      void* y, int dt, hipStream_t st) {
   if (!nchunks) return hipSuccess;
-  dim3 g = grid_for(nchunks), b(kThreads);
+  const int64_t n8 = nchunks * 4, per_block = (int64_t)kDeqUnits * kThreads;
+  dim3 g((unsigned)((n8 + per_block - 1) / per_block)), b(kThreads);
   if (dt == fp4impl::DT_F32)
-    k_dequant<FMT, H, fp4impl::DT_F32><<<g, b, 0, st>>>(codes, scales, ts, nchunks, y);
+    k_dequant<FMT, H, fp4impl::DT_F32><<<g, b, 0, st>>>(codes, scales, ts, n8, y);
   else
-    k_dequant<FMT, H, fp4impl::DT_BF16><<<g, b, 0, st>>>(codes, scales, ts, nchunks, y);
+    k_dequant<FMT, H, fp4impl::DT_BF16><<<g, b, 0, st>>>(codes, scales, ts, n8, y);
   return hipGetLastError();
 }
 
