@@ -24,7 +24,7 @@ concatenation [K primary | S residual] for codes and for scales.
 """
 import numpy as np
 
-from . import nvfp4
+from . import mxfp4, nvfp4
 from . import formats as F
 
 BLOCK = nvfp4.BLOCK
@@ -83,4 +83,54 @@ def dequantize(packed, scales, s_t, K, S):
     codes = F.unpack_nibbles(packed)
     p = nvfp4.dequantize_exact(codes[:, :K], scales[:, :K // BLOCK], s_t)
     r = nvfp4.dequantize_exact(codes[:, K:K + S], scales[:, K // BLOCK:], s_t)
+    return p, r
+
+
+def quantize_mx(x, perm, S, gamma=None, eps=1e-6, primary_scales=None, primary_codes=None,
+                residual_scales=None):
+    """MXFP4 flavour of the fused activation quantization, [K | S] layout.
+
+    The ARCQuant summary (Résultats Expérimentaux, Généralisabilité) reports that the
+    augmented-residual scheme extends to MXFP4; its Méthodologie items 2-3 give the two
+    stages.  Same steps as quantize() with MXFP4 in place of NVFP4: primary = MXFP4 (E8M0
+    per 32, oracle/mxfp4.py) of the reordered normalized z; residual = z - the exact value
+    of the primary quantization on the first S channels, quantized with its own E8M0
+    block scales.  There is no tensor scale.  S and K are multiples of 32.
+
+    Overrides replace decisions by given ones, as in quantize().  Returns `packed`
+    [M, (K+S)/2], `scales` [M, (K+S)/32] (E8M0), `z`, `residual_value`, and `primary` /
+    `residual` dicts with codes, scales, block maxima `amax` and element arguments.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    perm = np.asarray(perm, dtype=np.int64)
+    assert sorted(perm.tolist()) == list(range(K)), "perm must be a permutation of 0..K-1"
+    B = mxfp4.BLOCK
+    assert S % B == 0 and 0 <= S <= K and K % B == 0
+    z = rmsnorm(x, gamma, eps)[:, perm]
+    p = mxfp4.quantize(z, 0, primary_scales)
+    pc = p["codes"] if primary_codes is None else np.asarray(primary_codes, dtype=np.uint8).reshape(M, K)
+    xhat = mxfp4.dequantize_exact(pc, p["scales"])
+    r = z[:, :S] - xhat[:, :S]
+    if S > 0:
+        q = mxfp4.quantize(r, 0, residual_scales)
+        rc, rs, ramax, rarg = q["codes"], q["scales"], q["amax"], q["elem_arg"]
+    else:
+        rc = np.zeros((M, 0), np.uint8)
+        rs = np.zeros((M, 0), np.uint8)
+        ramax = rarg = np.zeros((M, 0))
+    codes = np.concatenate([pc, rc], axis=1)
+    scales = np.concatenate([p["scales"], rs], axis=1)
+    return dict(packed=F.pack_nibbles(codes), codes=codes, scales=scales.astype(np.uint8), z=z,
+                residual_value=r,
+                primary=dict(codes=pc, scales=p["scales"], amax=p["amax"], elem_arg=p["elem_arg"]),
+                residual=dict(codes=rc, scales=rs, amax=ramax, elem_arg=rarg))
+
+
+def dequantize_mx(packed, scales, K, S):
+    """Real values of the MXFP4 primary [M, K] and residual [M, S] parts (float64, exact)."""
+    codes = F.unpack_nibbles(packed)
+    B = mxfp4.BLOCK
+    p = mxfp4.dequantize_exact(codes[:, :K], scales[:, :K // B])
+    r = mxfp4.dequantize_exact(codes[:, K:K + S], scales[:, K // B:])
     return p, r

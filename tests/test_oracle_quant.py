@@ -287,6 +287,55 @@ def test_arcquant_zero_residual_channels_and_identity_perm():
     assert np.array_equal(r0["codes"], n["codes"]) and np.array_equal(r0["scales"], n["scales"])
 
 
+def test_arcquant_mx_against_exact_bruteforce():
+    """MXFP4 flavour: E8M0 per 32 on z, residual against the exact primary value."""
+    x, perm, S = _arc_case(seed=46, M=3, K=128, S=64)
+    r = arcquant.quantize_mx(x, perm, S)
+    z = r["z"]
+    assert np.array_equal(z, arcquant.rmsnorm(x)[:, perm])
+    for i in range(z.shape[0]):
+        zr = [Fr(float(v)) for v in z[i]]
+        pcodes, pscales = [], []
+        for b in range(0, 128, 32):
+            e, c = X.mxfp4_block_codes(zr[b:b + 32])
+            pscales.append(e)
+            pcodes += c
+        assert r["primary"]["codes"][i].tolist() == pcodes
+        assert r["primary"]["scales"][i].tolist() == pscales
+        res = [zr[j] - X.e2m1_value(pcodes[j]) * Fr(2) ** (pscales[j // 32] - 127) for j in range(S)]
+        assert np.allclose(r["residual_value"][i], [float(v) for v in res], rtol=0, atol=1e-15)
+        rcodes, rscales = [], []
+        for b in range(0, S, 32):
+            e, c = X.mxfp4_block_codes(res[b:b + 32])
+            rscales.append(e)
+            rcodes += c
+        assert r["residual"]["codes"][i].tolist() == rcodes
+        assert r["residual"]["scales"][i].tolist() == rscales
+    assert r["codes"].shape == (3, 128 + S) and r["scales"].shape == (3, (128 + S) // 32)
+
+
+def test_arcquant_mx_residual_reduces_error_and_gemm_linearity():
+    x, perm, S = _arc_case(seed=47, M=16, K=256, S=64)
+    r = arcquant.quantize_mx(x, perm, S)
+    p, rr = arcquant.dequantize_mx(r["packed"], r["scales"], 256, S)
+    e1 = np.abs(r["z"][:, :S] - p[:, :S])
+    e2 = np.abs(r["z"][:, :S] - p[:, :S] - rr)
+    assert np.all(e2 <= e1 + 1e-12)            # 0 is a grid point; saturation stays below |r|
+    assert e2.sum() < 0.5 * e1.sum()
+    w = np.random.default_rng(48).standard_normal((5, 256))
+    ext = np.concatenate([p, rr], axis=1) @ np.concatenate([w, w[:, :S]], axis=1).T
+    assert np.allclose(ext, p @ w.T + rr @ w[:, :S].T, rtol=1e-12, atol=1e-12)
+    exact = r["z"] @ w.T
+    assert np.linalg.norm(ext - exact) < np.linalg.norm(p @ w.T - exact)
+
+
+def test_arcquant_mx_without_residual_is_plain_mxfp4():
+    x, _, _ = _arc_case(seed=49)
+    r0 = arcquant.quantize_mx(x, np.arange(128), 0)
+    m = mxfp4.quantize(arcquant.rmsnorm(x))
+    assert np.array_equal(r0["codes"], m["codes"]) and np.array_equal(r0["scales"], m["scales"])
+
+
 # ----------------------------------------------------------------------------- GEMM
 
 def test_gemm_against_exact_bruteforce():
