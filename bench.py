@@ -166,6 +166,69 @@ def run_w4a4_gemm(args):
     return out
 
 
+def run_arcquant_gemm(args):
+    """ARCQuant augmented GEMM: residual quantization (MXFP4) + one K+S GEMM, against the
+    same activation path without residual channels (S = 0) and a K GEMM."""
+    wl = W.WORKLOADS["arcquant_gemm"]
+    M, K = wl.shape
+    S, N = wl.extra["S"], wl.extra["N"]
+    x_cpu = W.arcquant_input()
+    x = x_cpu.to(DEV)
+    perm = torch.from_numpy(W.calibration_order(x_cpu)).to(DEV)
+    w = W.gemm_weights(N, K, wl.extra["weight_seed"], wl.extra["weight_std"]).to(DEV)
+    w_perm = w[:, perm.long()].contiguous()
+    del w
+    # offline: reordered weights, and the augmented copy with the first S columns repeated
+    b_base = fp4.fp4_quantize(w_perm, "mxfp4", 0)[:2]
+    b_aug = fp4.fp4_quantize(torch.cat([w_perm, w_perm[:, :S]], dim=1).contiguous(), "mxfp4", 0)[:2]
+    del w_perm
+    a_aug = (torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=DEV),
+             torch.empty((M, (K + S) // 32), dtype=torch.uint8, device=DEV))
+    a_base = (torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=DEV))
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+
+    def step(s_, a, b, tq=None, tg=None):
+        e = tq.start() if tq else None
+        fp4.fp4_residual_quantize_mx(x, perm, s_, codes=a[0], scales=a[1])
+        if tq:
+            tq.stop(e)
+            e = tg.start()
+        fp4.fp4_gemm(a[0], a[1], b[0], b[1], c=c)
+        if tg:
+            tg.stop(e)
+
+    res = {}
+    for name, s_, a, b in (("augmented", S, a_aug, b_aug), ("base", 0, a_base, b_base)):
+        for _ in range(args.warmup):
+            step(s_, a, b)
+        torch.cuda.synchronize()
+        tq, tg = Timer(), Timer()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(s_, a, b, tq, tg)
+        torch.cuda.synchronize()
+        res[name] = dict(ms=(time.perf_counter() - t0) * 1e3 / args.steps, quant_ms=tq.mean_ms(), gemm_ms=tg.mean_ms())
+    kk = K + S
+    gemm_tflops = 2.0 * M * N * kk / (res["augmented"]["gemm_ms"] * 1e-3) / 1e12
+    quant_bytes = M * K * 2 + K * 4 + M * kk // 2 + M * kk // 32
+    quant_gbs = quant_bytes / (res["augmented"]["quant_ms"] * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": 2.0 * M * N * K / (res["augmented"]["ms"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["augmented"]["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1/e8m0 (fp32 accumulate)",
+        "data": "synthetic", "config": {"workload": f"arcquant_gemm: {wl.description}", "M": M, "N": N, "K": K, "S": S},
+        "augmented_overhead": res["augmented"]["ms"] / res["base"]["ms"] - 1.0,
+        "steps_ms": res,
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / FP4_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm (K+S)",
+                     "kernel_ms": res["augmented"]["gemm_ms"], "flop_per_launch": 2.0 * M * N * kk},
+        "roofline_quantize": {"bound": "hbm", "achieved": quant_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": quant_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_arcquant<MX>",
+                              "kernel_ms": res["augmented"]["quant_ms"], "bytes_per_launch": quant_bytes},
+    }
+
+
 def _rotating(make, nbytes_per_set, min_total=1 << 30):
     sets = max(2, -(-min_total // max(nbytes_per_set, 1)))
     return [make() for _ in range(sets)]
@@ -332,6 +395,8 @@ def main():
     fp4.lib()                                   # fail loudly if the HIP library is missing
     if args.workload == "w4a4_gemm":
         out = run_w4a4_gemm(args)
+    elif args.workload == "arcquant_gemm":
+        out = run_arcquant_gemm(args)
     elif args.workload == "hbm_copy":
         out = run_hbm_copy(args)
     else:

@@ -109,6 +109,29 @@ fp4_status fp4_residual_quantize(const void* x, int64_t M, int64_t K, const floa
                                  void* stream);
 
 /*
+ * fp4_residual_quantize_mx -- MXFP4 flavour of fp4_residual_quantize: RMSNorm, channel
+ * reorder, primary MXFP4 and residual MXFP4 of the first S reordered channels.
+ *
+ * Defined by the ARCQuant summary (gist.science/fr/paper/2601.07475): Méthodologie
+ * items 1-3 for the steps, Résultats Expérimentaux (Généralisabilité) for the extension
+ * of the augmented-residual scheme to MXFP4.  Per 32-channel block of z: E8M0 scale
+ * 2^(floor(log2 amax) - 2), codes E2M1_RNE(z / scale); residual r = z - (primary value)
+ * on the first S channels, quantized the same way with its own scales.  No tensor scale.
+ * The output feeds fp4_gemm directly with K' = K + S against weights whose columns are
+ * reordered by `perm` and whose first S reordered columns are repeated after them.
+ *
+ *   x, gamma, eps, perm   as for fp4_residual_quantize
+ *   S            residual channels, S % 32 == 0, S <= K
+ *   codes        [M][(K+S)/2] output: K/2 primary bytes then S/2 residual bytes per row
+ *   scales       [M][(K+S)/32] output E8M0: K/32 primary then S/32 residual
+ *   dbg_normed   optional [M][K] fp32 output of the normalized, reordered values z
+ * Shapes: K % 32 == 0, 32 <= K <= 16384.  perm must be a permutation (not checked).
+ */
+fp4_status fp4_residual_quantize_mx(const void* x, int64_t M, int64_t K, const float* gamma, float eps,
+                                    const int32_t* perm, int64_t S, uint8_t* codes, uint8_t* scales,
+                                    float* dbg_normed, void* stream);
+
+/*
  * fp4_pack_bytes -- HOST function, no device work: size in bytes of the packed
  * dual-scale message of an [M][K] tensor (K % 128 == 0), or 0 for invalid sizes.
  *

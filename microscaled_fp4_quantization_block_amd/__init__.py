@@ -7,5 +7,5 @@ the library; the first call does, and fails loudly if it has not been built.
 """
 from .binding import (  # noqa: F401
     Fp4Error, fp4_dequantize, fp4_gemm, fp4_pack, fp4_pack_bytes, fp4_quantize,
-    fp4_residual_quantize, fp4_unpack, lib, library_path,
+    fp4_residual_quantize, fp4_residual_quantize_mx, fp4_unpack, lib, library_path,
 )

@@ -18,7 +18,7 @@ FP4_SCALE_COMPUTE, FP4_SCALE_GIVEN = 0, 1
 _STATUS = {0: "FP4_OK", 1: "FP4_E_NULL", 2: "FP4_E_SHAPE", 3: "FP4_E_ALIGN",
            4: "FP4_E_UNSUPPORTED", 5: "FP4_E_HIP"}
 #: every symbol include/fp4.h declares
-EXPORTED = ("fp4_quantize", "fp4_dequantize", "fp4_residual_quantize", "fp4_pack_bytes",
+EXPORTED = ("fp4_quantize", "fp4_dequantize", "fp4_residual_quantize", "fp4_residual_quantize_mx", "fp4_pack_bytes",
             "fp4_pack", "fp4_unpack", "fp4_gemm", "fp4_status_str", "fp4_last_error")
 
 _lib = None
@@ -45,6 +45,7 @@ def lib():
         L.fp4_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, i32, vp, vp]
         L.fp4_dequantize.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, i32, vp]
         L.fp4_residual_quantize.argtypes = [vp, i64, i64, vp, f32, vp, i64, vp, vp, vp, i32, vp, vp]
+        L.fp4_residual_quantize_mx.argtypes = [vp, i64, i64, vp, f32, vp, i64, vp, vp, vp, vp]
         L.fp4_pack_bytes.argtypes = [i64, i64]
         L.fp4_pack_bytes.restype = ctypes.c_size_t
         L.fp4_pack.argtypes = [vp, i64, i64, vp, vp, vp]
@@ -54,7 +55,7 @@ def lib():
         L.fp4_status_str.restype = ctypes.c_char_p
         L.fp4_last_error.argtypes = []
         L.fp4_last_error.restype = ctypes.c_char_p
-        for name in ("fp4_quantize", "fp4_dequantize", "fp4_residual_quantize", "fp4_pack",
+        for name in ("fp4_quantize", "fp4_dequantize", "fp4_residual_quantize", "fp4_residual_quantize_mx", "fp4_pack",
                      "fp4_unpack", "fp4_gemm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -149,6 +150,24 @@ def fp4_residual_quantize(x, perm, S, gamma=None, eps=1e-6, codes=None, scales=N
                                        _ptr(codes), _ptr(scales), _ptr(tensor_scale), m,
                                        _ptr(dbg_normed), _stream(stream)))
     return codes, scales, tensor_scale
+
+
+def fp4_residual_quantize_mx(x, perm, S, gamma=None, eps=1e-6, codes=None, scales=None,
+                             dbg_normed=None, stream=None):
+    """MXFP4 flavour of the ARCQuant fused kernel on bf16 x [M, K].
+
+    Returns (codes [M, (K+S)/2], scales [M, (K+S)/32] E8M0)."""
+    _dev(x, "x")
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, (K + S) // 32), dtype=torch.uint8, device=x.device)
+    if perm.dtype != torch.int32:
+        raise ValueError("perm must be int32")
+    _check(lib().fp4_residual_quantize_mx(_ptr(x), M, K, _ptr(gamma), float(eps), _ptr(perm), int(S),
+                                          _ptr(codes), _ptr(scales), _ptr(dbg_normed), _stream(stream)))
+    return codes, scales
 
 
 def fp4_pack_bytes(M, K):

@@ -134,6 +134,30 @@ fp4_status fp4_residual_quantize(const void* x, int64_t M, int64_t K, const floa
   return hip_status(e, "fp4_residual_quantize");
 }
 
+fp4_status fp4_residual_quantize_mx(const void* x, int64_t M, int64_t K, const float* gamma, float eps,
+                                    const int32_t* perm, int64_t S, uint8_t* codes, uint8_t* scales,
+                                    float* dbg_normed, void* stream) {
+  REQUIRE(M >= 0, FP4_E_SHAPE, "fp4_residual_quantize_mx: negative M");
+  REQUIRE(K >= 32 && K <= 16384 && K % 32 == 0, FP4_E_SHAPE,
+          "fp4_residual_quantize_mx: K=%lld must be a multiple of 32 in [32, 16384]", (long long)K);
+  REQUIRE(S >= 0 && S <= K && S % 32 == 0, FP4_E_SHAPE,
+          "fp4_residual_quantize_mx: S=%lld must be a multiple of 32 in [0, K]", (long long)S);
+  REQUIRE(eps >= 0.0f, FP4_E_SHAPE, "fp4_residual_quantize_mx: eps must be >= 0");
+  REQUIRE(perm != nullptr, FP4_E_NULL, "fp4_residual_quantize_mx: perm is required");
+  REQUIRE(aligned(perm, 4) && (!gamma || aligned(gamma, 4)), FP4_E_ALIGN,
+          "fp4_residual_quantize_mx: perm/gamma misaligned");
+  if (M > 0) {
+    REQUIRE(x && codes && scales, FP4_E_NULL, "fp4_residual_quantize_mx: x, codes and scales are required");
+    REQUIRE(aligned(x, 16) && aligned(codes, 16), FP4_E_ALIGN,
+            "fp4_residual_quantize_mx: x and codes must be 16-byte aligned");
+    REQUIRE(!dbg_normed || aligned(dbg_normed, 16), FP4_E_ALIGN, "fp4_residual_quantize_mx: dbg_normed misaligned");
+  }
+  hipError_t e = fp4impl::launch_residual_quantize_mx(reinterpret_cast<const uint16_t*>(x), M, K, gamma, eps, perm,
+                                                      S, codes, scales, dbg_normed,
+                                                      reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "fp4_residual_quantize_mx");
+}
+
 size_t fp4_pack_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0 || K % 128 != 0) return 0;
   return fp4impl::pack_layout(M, K).total;

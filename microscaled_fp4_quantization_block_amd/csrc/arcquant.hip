@@ -208,6 +208,54 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
   }
 }
 
+// MXFP4 flavour: 32-channel blocks, one E8M0 scale per block (floor(log2 amax) - 2), codes
+// by the hardware convert (exact: power-of-two scale).  The residual z - V 2^(e-127) is
+// exact in binary32: z lies within a factor of two of its nearest grid point, or the
+// grid point is 0.  Lane l takes blocks l, l + 64, ...
+__device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
+                                              int lane, float inv_rms, const float* __restrict__ gamma,
+                                              uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                              float* __restrict__ dbg) {
+  const int nblk = K / 32, sblk = S / 32;
+  const int64_t row_codes = (K + S) / 2, row_scales = (K + S) / 32;
+  uint8_t* crow = codes + r * row_codes;
+  uint8_t* srow = scales + r * row_scales;
+  for (int b = lane; b < nblk; b += 64) {
+    uint4 pw4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pw4[q] = reinterpret_cast<const uint4*>(ps)[4 * b + q];
+    float z[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w[4] = {pw4[q].x, pw4[q].y, pw4[q].z, pw4[q].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c0 = (int)(w[k] & 0xFFFFu), c1 = (int)(w[k] >> 16);
+        z[8 * q + 2 * k] = norm_value(xs[c0], inv_rms, gamma, c0);
+        z[8 * q + 2 * k + 1] = norm_value(xs[c1], inv_rms, gamma, c1);
+      }
+    }
+    if (dbg) store_f32<32>(dbg + r * K + 32 * b, z);
+    const uint32_t e = e8m0_from_amax(absmax<32>(z));
+    const float sc = e8m0_value(e);
+    const uint4 w = e2m1_encode32(z, sc);
+    *reinterpret_cast<uint4*>(crow + 16 * b) = w;
+    srow[b] = (uint8_t)e;
+    if (b < sblk) {
+      float q[32];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e2m1_decode8(ws[i], sc, q + 8 * i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) q[i] = z[i] - q[i];
+      const uint32_t er = e8m0_from_amax(absmax<32>(q));
+      *reinterpret_cast<uint4*>(crow + K / 2 + 16 * b) = e2m1_encode32(q, e8m0_value(er));
+      srow[nblk + b] = (uint8_t)er;
+    }
+  }
+}
+
+template <int FMT>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
            const int32_t* __restrict__ perm, int S, uint8_t* __restrict__ codes,
@@ -222,9 +270,15 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
   __syncthreads();
 
-  const float s_t = *tensor_scale;
+  const float s_t = FMT == fp4impl::FMT_NV ? *tensor_scale : 0.0f;
   const int units = K / 8;
   const int64_t stride = (int64_t)gridDim.x * W;
+  auto encode = [&](int64_t row, float inv_rms) {
+    if constexpr (FMT == fp4impl::FMT_NV)
+      encode_row(xs, ps, row, K, S, lane, inv_rms, gamma, s_t, codes, scales, dbg);
+    else
+      encode_row_mx(xs, ps, row, K, S, lane, inv_rms, gamma, codes, scales, dbg);
+  };
   int64_t r = (int64_t)blockIdx.x * W + wave;
   if (units <= 64 * kUnroll) {
     // whole row in one chunk: the next row's loads are in flight while this row is encoded
@@ -234,14 +288,14 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
       const float ss = wave_sum(park_units(raw, 0, units, lane, xs, 0.0f));
       if (r + stride < M) load_units(x + (r + stride) * K, 0, units, lane, raw);
       wave_lds_sync();
-      encode_row(xs, ps, r, K, S, lane, inv_rms_of(ss, K, eps), gamma, s_t, codes, scales, dbg);
+      encode(r, inv_rms_of(ss, K, eps));
       wave_lds_sync();                                   // xs is refilled by the next row
     }
   } else {
     for (; r < M; r += stride) {
       const float ss = load_row(x + r * K, units, lane, xs);
       wave_lds_sync();
-      encode_row(xs, ps, r, K, S, lane, inv_rms_of(ss, K, eps), gamma, s_t, codes, scales, dbg);
+      encode(r, inv_rms_of(ss, K, eps));
       wave_lds_sync();
     }
   }
@@ -258,6 +312,26 @@ hipError_t allow_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+struct ArcLaunch {
+  int W, Wq;
+  unsigned grid, grid_q;
+  size_t lds_stats, lds_quant;
+};
+
+ArcLaunch arc_launch(int64_t M, int64_t K) {
+  ArcLaunch a;
+  a.W = waves_for(K);
+  const int64_t rows_per_grid = 1024 * (int64_t)a.W;     // at most 1024 workgroups, persistent beyond
+  a.grid = (unsigned)(M <= 0 ? 1 : (M < rows_per_grid ? (M + a.W - 1) / a.W : 1024));
+  const bool pipelined = K / 8 <= 64 * kUnroll;
+  a.Wq = pipelined ? kPipeWaves : a.W;
+  const int64_t wq_total = pipelined ? (M < kPipeTotal ? M : kPipeTotal) : (M < rows_per_grid ? M : rows_per_grid);
+  a.grid_q = (unsigned)(wq_total <= 0 ? 1 : (wq_total + a.Wq - 1) / a.Wq);
+  a.lds_stats = (size_t)2 * K * a.W;
+  a.lds_quant = (size_t)2 * K * (a.Wq + 1);
+  return a;
+}
+
 }  // namespace
 
 namespace fp4impl {
@@ -266,23 +340,30 @@ hipError_t launch_residual_quantize(const uint16_t* x, int64_t M, int64_t K, con
                                     float eps, const int32_t* perm, int64_t S, uint8_t* codes,
                                     uint8_t* scales, float* ts, bool compute, float* dbg,
                                     hipStream_t st) {
-  const int W = waves_for(K);
-  const int64_t rows_per_grid = 1024 * (int64_t)W;       // at most 1024 workgroups, persistent beyond
-  const unsigned grid = (unsigned)(M <= 0 ? 1 : (M < rows_per_grid ? (M + W - 1) / W : 1024));
-  const bool pipelined = K / 8 <= 64 * kUnroll;
-  const int Wq = pipelined ? kPipeWaves : W;
-  const int64_t wq_total = pipelined ? (M < kPipeTotal ? M : kPipeTotal) : (M < rows_per_grid ? M : rows_per_grid);
-  const unsigned grid_q = (unsigned)(wq_total <= 0 ? 1 : (wq_total + Wq - 1) / Wq);
-  const size_t lds_stats = (size_t)2 * K * W, lds_quant = (size_t)2 * K * (Wq + 1);
-  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arc_stats), lds_stats);
-  if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(k_arcquant), lds_quant);
+  const ArcLaunch a = arc_launch(M, K);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arc_stats), a.lds_stats);
+  if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT_NV>), a.lds_quant);
   if (e != hipSuccess) return e;
   if (compute) {
     k_zero_scalar<<<1, 1, 0, st>>>(ts);
-    if (M) k_arc_stats<<<grid, 64 * W, lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
+    if (M) k_arc_stats<<<a.grid, 64 * a.W, a.lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
     k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
-  if (M) k_arcquant<<<grid_q, 64 * Wq, lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes, scales, ts, dbg);
+  if (M)
+    k_arcquant<FMT_NV><<<a.grid_q, 64 * a.Wq, a.lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes,
+                                                               scales, ts, dbg);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_quantize_mx(const uint16_t* x, int64_t M, int64_t K, const float* gamma, float eps,
+                                       const int32_t* perm, int64_t S, uint8_t* codes, uint8_t* scales,
+                                       float* dbg, hipStream_t st) {
+  if (!M) return hipSuccess;
+  const ArcLaunch a = arc_launch(M, K);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT_MX>), a.lds_quant);
+  if (e != hipSuccess) return e;
+  k_arcquant<FMT_MX><<<a.grid_q, 64 * a.Wq, a.lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes,
+                                                             scales, nullptr, dbg);
   return hipGetLastError();
 }
 

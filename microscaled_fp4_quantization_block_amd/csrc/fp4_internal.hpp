@@ -24,6 +24,10 @@ hipError_t launch_residual_quantize(const uint16_t* x, int64_t M, int64_t K, con
                                     uint8_t* scales, float* tensor_scale, bool compute_scale,
                                     float* dbg, hipStream_t stream);
 
+hipError_t launch_residual_quantize_mx(const uint16_t* x, int64_t M, int64_t K, const float* gamma,
+                                       float eps, const int32_t* perm, int64_t S, uint8_t* codes,
+                                       uint8_t* scales, float* dbg, hipStream_t stream);
+
 struct PackLayout {
   size_t off_micro, off_group, total;
 };

@@ -50,6 +50,14 @@ WORKLOADS = {
         "fused RMSNorm + absmax channel reorder + NVFP4 primary + residual of top 256 "
         "channels: bf16 4096x4096 N(0,1), 64 outlier channels x30, K+S = 4352",
         (4096, 4096), 4, dict(outliers=64, outlier_gain=30.0, S=256, eps=1e-6)),
+    "arcquant_gemm": Workload(
+        "arcquant_gemm",
+        "ARCQuant augmented GEMM (MXFP4 flavour): bf16 4096x4096 activations N(0,1) with 64 "
+        "outlier channels x30, RMSNorm + reorder + MXFP4 primary + residual of the top 256 "
+        "channels, then the K+S = 4352 GEMM against 14336 reordered MXFP4 weight rows (first "
+        "256 reordered columns repeated) from N(0,0.02); compared with the same path at S = 0",
+        (4096, 4096), 4, dict(outliers=64, outlier_gain=30.0, S=256, eps=1e-6, N=14336, weight_seed=51,
+                              weight_std=0.02)),
     "w4a4_gemm": Workload(
         "w4a4_gemm",
         "W4A4 MXFP4 GEMM, Hadamard-32 activation quant on the fly: A bf16 8192x8192 "

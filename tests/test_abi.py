@@ -97,6 +97,15 @@ def test_other_entry_points_validation():
     assert _status("fp4_residual_quantize", *bad)[0] == 1
     bad = list(args); bad[2] = 32768                                   # K beyond the LDS row
     assert _status("fp4_residual_quantize", *bad)[0] == 2
+    mx = [FAKE, 4, 64, None, ctypes.c_float(1e-6), FAKE, 32, FAKE, FAKE, None, None]
+    bad = list(mx); bad[6] = 16                                        # S not a multiple of 32
+    assert _status("fp4_residual_quantize_mx", *bad)[0] == 2
+    bad = list(mx); bad[2] = 48                                        # K not a multiple of 32
+    assert _status("fp4_residual_quantize_mx", *bad)[0] == 2
+    bad = list(mx); bad[5] = None
+    assert _status("fp4_residual_quantize_mx", *bad)[0] == 1
+    bad = list(mx); bad[7] = FAKE + 8                                  # codes not 16-byte aligned
+    assert _status("fp4_residual_quantize_mx", *bad)[0] == 3
     assert _status("fp4_pack", FAKE, 4, 100, FAKE, None, None)[0] == 2
     assert _status("fp4_pack", FAKE, 4, 128, FAKE + 16, None, None)[0] == 3
     assert _status("fp4_unpack", None, 4, 128, FAKE, None)[0] == 1
@@ -112,4 +121,6 @@ def test_empty_shapes_are_no_ops():
     assert _status("fp4_quantize", None, 1, 0, 64, 1, 32, None, None, None, 0, None, None)[0] == 0
     assert _status("fp4_dequantize", None, None, None, 0, 64, 1, 0, None, 0, None)[0] == 0
     assert _status("fp4_pack", None, 0, 128, None, None, None)[0] == 0
+    assert _status("fp4_residual_quantize_mx", None, 0, 64, None, ctypes.c_float(1e-6), FAKE, 32, None, None,
+                   None, None)[0] == 0
     assert _status("fp4_gemm", None, None, None, None, 0, 5, 128, None, 1, None)[0] == 0
