@@ -229,6 +229,69 @@ def run_arcquant_gemm(args):
     }
 
 
+def _rel_mse(xhat, x):
+    d = xhat.double() - x.double()
+    return float((d * d).sum() / (x.double() * x.double()).sum())
+
+
+def format_errors(x, formats=("nvfp4", "mxfp4"), hadamards=(0, 16, 32), dualscale=True):
+    """Relative squared reconstruction error |x - deq(q(x))|^2 / |x|^2 of x [M, K] on the
+    GPU (library quantize + dequantize, inverse rotation applied), per format."""
+    out = {}
+    for fmt in formats:
+        for h in hadamards:
+            codes, scales, ts = fp4.fp4_quantize(x, fmt, h)
+            xhat = fp4.fp4_dequantize(codes, scales, ts, fmt, h, out_dtype=torch.float32)
+            out[f"{fmt}" + (f"+H{h}" if h else "")] = _rel_mse(xhat, x)
+    if dualscale and x.dtype == torch.bfloat16:
+        M, K = x.shape
+        out["dualscale+H128(16x8)"] = _rel_mse(fp4.fp4_unpack(fp4.fp4_pack(x), M, K), x)
+    return out
+
+
+def arcquant_errors(x, perm, S):
+    """Error of the normalized, reordered z against primary (+ residual) dequantization,
+    NVFP4 and MXFP4 flavours, and of plain NVFP4 / MXFP4 / rotated MXFP4 of the same z."""
+    M, K = x.shape
+    out = {}
+    z = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    codes, scales, ts = fp4.fp4_residual_quantize(x, perm, S, dbg_normed=z)
+    p = fp4.fp4_dequantize(codes[:, :K // 2].contiguous(), scales[:, :K // 16].contiguous(), ts, "nvfp4", 0,
+                           out_dtype=torch.float32)
+    r = fp4.fp4_dequantize(codes[:, K // 2:].contiguous(), scales[:, K // 16:].contiguous(), ts, "nvfp4", 0,
+                           out_dtype=torch.float32)
+    out["nvfp4 (primary only)"] = _rel_mse(p, z)
+    p[:, :S] += r
+    out[f"arcquant nvfp4 S={S}"] = _rel_mse(p, z)
+    codes, scales = fp4.fp4_residual_quantize_mx(x, perm, S)
+    p = fp4.fp4_dequantize(codes[:, :K // 2].contiguous(), scales[:, :K // 32].contiguous(), None, "mxfp4", 0,
+                           out_dtype=torch.float32)
+    r = fp4.fp4_dequantize(codes[:, K // 2:].contiguous(), scales[:, K // 32:].contiguous(), None, "mxfp4", 0,
+                           out_dtype=torch.float32)
+    out["mxfp4 (primary only)"] = _rel_mse(p, z)
+    p[:, :S] += r
+    out[f"arcquant mxfp4 S={S}"] = _rel_mse(p, z)
+    out.update({f"z: {k}": v for k, v in format_errors(z, dualscale=False).items()})
+    return out
+
+
+def run_format_study(args):
+    """Quantization error of the formats on the workloads' activation distributions."""
+    t0 = time.perf_counter()
+    table = {
+        "gaussian + 41 outlier channels x50 (bf16 4096x4096)": format_errors(W.mxfp4_h32_input().to(DEV)),
+        "student-t df=4 (bf16 8192x8192)": format_errors(W.student_t_input().to(DEV)),
+    }
+    xa = W.arcquant_input()
+    perm = torch.from_numpy(W.calibration_order(xa)).to(DEV)
+    table["rmsnorm'd gaussian + 64 outlier channels x30, reordered (4096x4096)"] = arcquant_errors(xa.to(DEV), perm, 256)
+    torch.cuda.synchronize()
+    return {"metric": "relative squared quantization error |x - deq(q(x))|^2 / |x|^2", "value": None,
+            "unit": "ratio", "n_gpus": 1, "steps": 1, "warmup": 0, "ms_per_step": (time.perf_counter() - t0) * 1e3,
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp32 arithmetic",
+            "data": "synthetic", "config": {"workload": "format_study"}, "errors": table}
+
+
 def _rotating(make, nbytes_per_set, min_total=1 << 30):
     sets = max(2, -(-min_total // max(nbytes_per_set, 1)))
     return [make() for _ in range(sets)]
@@ -381,7 +444,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="w4a4_gemm", choices=sorted(W.WORKLOADS) + ["hbm_copy"])
+    ap.add_argument("--workload", default="w4a4_gemm", choices=sorted(W.WORKLOADS) + ["hbm_copy", "format_study"])
     ap.add_argument("--op", default="quant", choices=["quant", "dequant"],
                     help="memory workloads: time the forward op (quantize / pack) or its inverse")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -397,6 +460,8 @@ def main():
         out = run_w4a4_gemm(args)
     elif args.workload == "arcquant_gemm":
         out = run_arcquant_gemm(args)
+    elif args.workload == "format_study":
+        out = run_format_study(args)
     elif args.workload == "hbm_copy":
         out = run_hbm_copy(args)
     else:
