@@ -35,9 +35,14 @@
 //   id is remapped to give every XCD a contiguous band of tiles, walked in groups of 8
 //   tile-rows, keeping each XCD's L2 working set to a few A and B panels.
 // - When K is a multiple of 512, each tile starts its walk over K at a buffer offset set
-//   by its tile coordinates and wraps around: tiles that run together then read different
-//   K columns of their panels at any moment, which spreads the load over memory channels.
-//   Only the fp32 summation order changes.
+//   by its tile row and wraps around: the tiles that share an A panel stay in step (one
+//   stream of A per panel through L2), while tiles of different rows read different K
+//   columns at any moment, which spreads the load over memory channels.  Only the fp32
+//   summation order changes.
+// - bf16 output (N % 8 == 0) leaves through LDS: the accumulators are written as bf16 into
+//   the drained code buffers (16-byte chunks XOR-swizzled by row), then every wave stores
+//   two full 512-byte tile rows per instruction, instead of 8 bytes per lane scattered
+//   over 32 rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -348,7 +353,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
     }
     L.wave = wave;
     L.np = np;
-    L.rot = (K % (2 * BKP) == 0) ? (2 * (tile.m0 / BM + tile.n0 / BN)) % np : 0;
+    L.rot = (K % (2 * BKP) == 0) ? (2 * (tile.m0 / BM)) % np : 0;
   }
 
   const int wm = (wave / Cfg<NW>::WN) * (32 * TI), wn = (wave % Cfg<NW>::WN) * (32 * TJ);
@@ -364,6 +369,40 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
   k_loop<NW>(acc, L, np, ragged, codes[0], codes[1], scales[0], scales[1], wm, wn, r32, khalf);
 
   // epilogue: lane holds C[m][n0 .. n0+3] for m = row r32 of A-block i, n0 = 8 g + 4 khalf in B-block j
+  if (ctype == fp4impl::DT_BF16 && (N & 7) == 0) {
+    // every LDS DMA (including the out-of-range ones past the end) has landed and every
+    // wave is done with the code buffers
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    uint8_t* ct = codes[0];                      // [256 rows][512 bytes] of bf16, 128 KiB
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = wm + 32 * i + r32;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int byte = 2 * (wn + 32 * j + 8 * g + 4 * khalf);
+          const int pos = (((byte >> 4) ^ (m & 15)) << 4) | (byte & 15);
+          *reinterpret_cast<uint2*>(ct + m * 512 + pos) =
+              make_uint2(fp4dev::pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                         fp4dev::pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        }
+      }
+    }
+    __syncthreads();
+    // thread t: 16-byte chunk t % 32 of rows t / 32 + (2 NW) k
+    const int c = tid & 31;
+    uint16_t* C16 = reinterpret_cast<uint16_t*>(C);
+#pragma unroll
+    for (int k = 0; k < BM / (2 * NW); ++k) {
+      const int m = (tid >> 5) + 2 * NW * k;
+      const uint4 v = *reinterpret_cast<const uint4*>(ct + m * 512 + ((c ^ (m & 15)) << 4));
+      const int gm = tile.m0 + m, gn = tile.n0 + 8 * c;
+      if (gm < M && gn < N) *reinterpret_cast<uint4*>(C16 + (int64_t)gm * N + gn) = v;
+    }
+    return;
+  }
   const bool vec_ok = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
