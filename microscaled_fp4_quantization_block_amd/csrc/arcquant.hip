@@ -138,11 +138,10 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
 // first S channels the residual z - V s_b s_t and its codes and scale.
 __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K, int nblk, int sblk, float s_t,
                                              uint8_t* __restrict__ crow, uint8_t* __restrict__ srow) {
-  const uint32_t sb = nvfp4_block_scale(absmax<16>(z), s_t);
+  const float inv6s = recip_fast(6.0f * s_t);
+  const uint32_t sb = nvfp4_block_scale_fast(absmax<16>(z), inv6s);
   const float sbv = e4m3_value(sb);
-  const float S32 = sbv * s_t;
-  const float E = S32 > 0.0f ? 1.0f / S32 : 0.0f;
-  const uint2 w = nvfp4_encode16_fast(z, E);
+  const uint2 w = nvfp4_encode16_fast(z, recip_fast(sbv * s_t));
   *reinterpret_cast<uint2*>(crow + 8 * b) = w;
   srow[b] = (uint8_t)sb;
   if (b < sblk) {
@@ -151,10 +150,8 @@ __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K,
     e2m1_decode8(w.y, 1.0f, q + 8);
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, z[i]);   // z - V s_b s_t
-    const uint32_t sr = nvfp4_block_scale(absmax<16>(q), s_t);
-    const float R32 = e4m3_value(sr) * s_t;
-    const float Er = R32 > 0.0f ? 1.0f / R32 : 0.0f;
-    *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, Er);
+    const uint32_t sr = nvfp4_block_scale_fast(absmax<16>(q), inv6s);
+    *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t));
     srow[nblk + b] = (uint8_t)sr;
   }
 }

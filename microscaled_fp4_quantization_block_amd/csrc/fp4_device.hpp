@@ -245,6 +245,23 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float s_t) {
   return e4m3_rne((double)amax / (6.0 * (double)s_t));
 }
 
+// Fast scale arithmetic for paths whose inputs already carry fp32 rounding (rotated or
+// normalised values): decisions may move only where the exact argument lies within a
+// few binary32 ulps of a boundary.
+//   recip_fast       1/x by v_rcp_f32 (about 1 ulp), 0 for x <= 0
+//   e4m3_fast        E4M3 code of q >= 0 by the hardware convert (OCP E4M3, nearest-even;
+//                    matches the float64 rule on every value up to 448), clamped at 448
+//   nvfp4_block_scale_fast   E4M3(amax * inv6s) with inv6s = recip_fast(6 s)
+__device__ __forceinline__ float recip_fast(float x) { return x > 0.0f ? __builtin_amdgcn_rcpf(x) : 0.0f; }
+
+__device__ __forceinline__ uint32_t e4m3_fast(float q) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(q, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t nvfp4_block_scale_fast(float amax, float inv6s) {
+  return e4m3_fast(amax * inv6s);
+}
+
 // --------------------------------------------------------------------------- E8M0
 
 // MX scale code of a block maximum: floor(log2 amax) - 2 + 127, clamped to [0, 254];

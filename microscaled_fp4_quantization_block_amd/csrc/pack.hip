@@ -11,7 +11,9 @@
 //             c = +-1, which leaves its result multiplied by (-1)^popcount(p); that sign
 //             is folded into the 1/sqrt(128) normalisation.
 // Group scale fl32(amax/2688) per 128, E4M3 micro scale per 16, E2M1 codes; the message
-// is planar: codes | micro scales | group scales, each section 256-byte aligned.
+// is planar: codes | micro scales | group scales, each section 256-byte aligned.  The
+// values are rotated (fp32-rounded), so the scale and element decisions take the fast
+// reciprocal-and-convert route.
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
 
@@ -58,15 +60,14 @@ k_pack(const uint16_t* x, int64_t nchunks, uint8_t* codes, uint8_t* micro, float
   float m = absmax<32>(v);
   m = quad_max<kQuadXor1>(m);
   m = quad_max<kQuadXor2>(m);
-  const float s_g = m / 2688.0f;       // correctly rounded fp32 division
+  const float s_g = m / 2688.0f;       // correctly rounded fp32 division (stored)
+  const float inv6s = recip_fast(6.0f * s_g);
   uint2 w[2];
   uint32_t sm[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    sm[h] = nvfp4_block_scale(absmax<16>(v + 16 * h), s_g);
-    float S32 = e4m3_value(sm[h]) * s_g;
-    float E = S32 > 0.0f ? 1.0f / S32 : 0.0f;
-    w[h] = nvfp4_encode16_fast(v + 16 * h, E);
+    sm[h] = nvfp4_block_scale_fast(absmax<16>(v + 16 * h), inv6s);
+    w[h] = nvfp4_encode16_fast(v + 16 * h, recip_fast(e4m3_value(sm[h]) * s_g));
   }
   reinterpret_cast<uint4*>(codes)[c] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
   reinterpret_cast<uint16_t*>(micro)[c] = (uint16_t)(sm[0] | (sm[1] << 8));

@@ -62,8 +62,8 @@ k_quant_mx(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales, floa
   scales[c] = (uint8_t)e;
 }
 
-// NVFP4: two 16-blocks per chunk.  Unrotated input takes the exact element decision;
-// rotated input (already fp32-rounded) the fast one.
+// NVFP4: two 16-blocks per chunk.  Unrotated input takes the exact scale and element
+// decisions (float64 quotients); rotated input (already fp32-rounded) the fast ones.
 template <int DT, int H>
 __global__ void __launch_bounds__(kThreads)
 k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
@@ -77,17 +77,17 @@ k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
   if (dbg) store_f32<32>(dbg + c * 32, v);
   uint2 w[2];
   uint32_t sb[2];
+  const float inv6s = recip_fast(6.0f * s_t);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    sb[b] = nvfp4_block_scale(absmax<16>(v + 16 * b), s_t);
+    sb[b] = H == 0 ? nvfp4_block_scale(absmax<16>(v + 16 * b), s_t)
+                   : nvfp4_block_scale_fast(absmax<16>(v + 16 * b), inv6s);
     if constexpr (H == 0) {
       double S = (double)e4m3_value(sb[b]) * (double)s_t;     // exact
       double R = S > 0.0 ? 1.0 / S : 0.0;
       w[b] = nvfp4_encode16_exact(v + 16 * b, R);
     } else {
-      float S32 = e4m3_value(sb[b]) * s_t;
-      float E = S32 > 0.0f ? 1.0f / S32 : 0.0f;
-      w[b] = nvfp4_encode16_fast(v + 16 * b, E);
+      w[b] = nvfp4_encode16_fast(v + 16 * b, recip_fast(e4m3_value(sb[b]) * s_t));
     }
   }
   reinterpret_cast<uint4*>(codes)[c] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
