@@ -221,10 +221,12 @@ def run_arcquant_gemm(args):
         "augmented_overhead": res["augmented"]["ms"] / res["base"]["ms"] - 1.0,
         "steps_ms": res,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / FP4_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm (K+S)",
+                     "frac": gemm_tflops / FP4_PEAK_TFLOPS, "traffic": _traffic("arcquant_gemm_gemm"),
+                     "kernel": "k_gemm (K+S)",
                      "kernel_ms": res["augmented"]["gemm_ms"], "flop_per_launch": 2.0 * M * N * kk},
         "roofline_quantize": {"bound": "hbm", "achieved": quant_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": quant_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_arcquant<MX>",
+                              "frac": quant_gbs / HBM_PEAK_GBS, "traffic": _traffic("arcquant_mx_quant"),
+                              "kernel": "k_arcquant<MX>",
                               "kernel_ms": res["augmented"]["quant_ms"], "bytes_per_launch": quant_bytes},
     }
 
