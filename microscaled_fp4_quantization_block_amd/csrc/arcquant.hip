@@ -263,24 +263,27 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   uint16_t* ps = smem;                                   // [K] permutation (16-bit)
   uint16_t* xs = smem + (size_t)(1 + wave) * K;          // [K] this wave's row
 
+  const int units = K / 8;
+  const int64_t stride = (int64_t)gridDim.x * W;
+  int64_t r = (int64_t)blockIdx.x * W + wave;
+  const bool pipelined = units <= 64 * kUnroll;
+  // the first row's loads go out before the permutation is staged, so both are in flight
+  uint4 raw[kUnroll];
+  if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
+
   // an index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced
   for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
   __syncthreads();
 
   const float s_t = FMT == fp4impl::FMT_NV ? *tensor_scale : 0.0f;
-  const int units = K / 8;
-  const int64_t stride = (int64_t)gridDim.x * W;
   auto encode = [&](int64_t row, float inv_rms) {
     if constexpr (FMT == fp4impl::FMT_NV)
       encode_row(xs, ps, row, K, S, lane, inv_rms, gamma, s_t, codes, scales, dbg);
     else
       encode_row_mx(xs, ps, row, K, S, lane, inv_rms, gamma, codes, scales, dbg);
   };
-  int64_t r = (int64_t)blockIdx.x * W + wave;
-  if (units <= 64 * kUnroll) {
+  if (pipelined) {
     // whole row in one chunk: the next row's loads are in flight while this row is encoded
-    uint4 raw[kUnroll];
-    if (r < M) load_units(x + r * K, 0, units, lane, raw);
     for (; r < M; r += stride) {
       const float ss = wave_sum(park_units(raw, 0, units, lane, xs, 0.0f));
       if (r + stride < M) load_units(x + (r + stride) * K, 0, units, lane, raw);
