@@ -187,6 +187,36 @@ def test_nvfp4_rotated(h):
     P.assert_values_close(_np(y), want, h, what="dequantized + inverse H")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("h", [0, 16, 32])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_dequantize_every_variant(fmt, h, out):
+    """Dequantization of the GPU's own codes against the oracle's dequantization of the same
+    codes, for every format, rotation and output type, on a shape whose unit count leaves a
+    partial last workgroup (37 x 224)."""
+    _log(f"dequant {fmt} H{h} {out}")
+    rng = np.random.default_rng(7 + h)
+    x = rng.standard_normal((37, 224))
+    x[:, 9] *= 30
+    xg = W.to_bf16(x).to(DEV)
+    codes, scales, ts = fp4.fp4_quantize(xg, fmt, 0)
+    y = fp4.fp4_dequantize(codes, scales, ts, fmt, h, out)
+    if fmt == "nvfp4":
+        want = nvfp4.dequantize(_np(codes), _np(scales), _np(ts)[0], inverse_hadamard=h)
+    else:
+        want = mxfp4.dequantize(_np(codes), _np(scales), inverse_hadamard=h)
+    got = _vals(y.cpu())
+    if h == 0 and out == torch.float32:
+        assert np.array_equal(got, want.astype(np.float32).astype(np.float64))
+    elif h == 0:
+        bits = _np(y.view(torch.int16)).view(np.uint16)
+        assert np.array_equal(bits, F.f32_to_bf16_bits(want.astype(np.float32)))
+    elif out == torch.float32:
+        P.assert_values_close(got, want, h, what="dequantized + inverse H")
+    else:
+        P.assert_bf16_close(got, want, h, what="dequantized + inverse H, bf16")
+
+
 # ----------------------------------------------------------------------------- robustness
 
 def test_determinism_and_poisoned_outputs():
