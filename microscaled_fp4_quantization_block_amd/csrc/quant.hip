@@ -36,7 +36,7 @@ __global__ void k_finalize_tensor_scale(float* p) { *p = *p / kTensorDivisor; }
 // Per-tensor maximum of |H x| (running atomic max into *amax, which starts at 0).
 template <int DT, int H>
 __global__ void __launch_bounds__(kThreads) k_amax(const void* x, int64_t nchunks, float* amax) {
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   float m = 0.0f;
   if (c < nchunks) {
     float v[32];
@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* x, int64_t nchunk
 template <int DT, int H>
 __global__ void __launch_bounds__(kThreads)
 k_quant_mx(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales, float* dbg) {
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= nchunks) return;
   float v[32];
   load_chunk<DT>(x, c, v);
@@ -68,7 +68,7 @@ template <int DT, int H>
 __global__ void __launch_bounds__(kThreads)
 k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
            const float* tensor_scale, float* dbg) {
-  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= nchunks) return;
   const float s_t = *tensor_scale;
   float v[32];
@@ -104,12 +104,12 @@ constexpr int kDeqUnits = 4;
 template <int FMT, int H, int OUT>
 __global__ void __launch_bounds__(kThreads)
 k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t n8, void* y) {
-  const int64_t base = (int64_t)blockIdx.x * (kDeqUnits * kThreads) + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (kDeqUnits * blockDim.x) + threadIdx.x;
   const int p = threadIdx.x & 3;
   uint32_t cw[kDeqUnits], sc[kDeqUnits];
 #pragma unroll
   for (int u = 0; u < kDeqUnits; ++u) {
-    const int64_t i = base + (int64_t)u * kThreads;
+    const int64_t i = base + (int64_t)u * blockDim.x;
     const bool ok = i < n8;
     cw[u] = ok ? reinterpret_cast<const uint32_t*>(codes)[i] : 0u;
     sc[u] = ok ? (uint32_t)scales[FMT == fp4impl::FMT_MX ? (i >> 2) : (i >> 1)] : 0u;
@@ -117,7 +117,7 @@ k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale
   const float s_t = FMT == fp4impl::FMT_MX ? 0.0f : *tensor_scale;
 #pragma unroll
   for (int u = 0; u < kDeqUnits; ++u) {
-    const int64_t i = base + (int64_t)u * kThreads;
+    const int64_t i = base + (int64_t)u * blockDim.x;
     float v[8];
     if constexpr (FMT == fp4impl::FMT_MX) {
       e2m1_decode8(cw[u], e8m0_value(sc[u]), v);
@@ -137,12 +137,18 @@ k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale
   }
 }
 
-inline dim3 grid_for(int64_t nchunks) { return dim3((unsigned)((nchunks + kThreads - 1) / kThreads)); }
+// Small tensors get 64-thread workgroups, so that their few thousand lanes still spread
+// over many CUs (256-thread groups would leave most of the chip idle below ~4M elements).
+inline int threads_for(int64_t nchunks) { return nchunks < 16384 ? 64 : kThreads; }
+inline dim3 grid_for(int64_t nchunks) {
+  const int t = threads_for(nchunks);
+  return dim3((unsigned)((nchunks + t - 1) / t));
+}
 
 template <int DT, int H>
 hipError_t quantize_t(const void* x, int64_t nchunks, int fmt, uint8_t* codes, uint8_t* scales,
                       float* ts, bool compute, float* dbg, hipStream_t st) {
-  dim3 g = grid_for(nchunks), b(kThreads);
+  dim3 g = grid_for(nchunks), b(threads_for(nchunks));
   if (fmt == fp4impl::FMT_MX) {
     if (nchunks) k_quant_mx<DT, H><<<g, b, 0, st>>>(x, nchunks, codes, scales, dbg);
     return hipGetLastError();
@@ -160,8 +166,9 @@ template <int FMT, int H>
 hipError_t dequant_t(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t nchunks,
                      void* y, int dt, hipStream_t st) {
   if (!nchunks) return hipSuccess;
-  const int64_t n8 = nchunks * 4, per_block = (int64_t)kDeqUnits * kThreads;
-  dim3 g((unsigned)((n8 + per_block - 1) / per_block)), b(kThreads);
+  const int t = threads_for(nchunks);
+  const int64_t n8 = nchunks * 4, per_block = (int64_t)kDeqUnits * t;
+  dim3 g((unsigned)((n8 + per_block - 1) / per_block)), b(t);
   if (dt == fp4impl::DT_F32)
     k_dequant<FMT, H, fp4impl::DT_F32><<<g, b, 0, st>>>(codes, scales, ts, n8, y);
   else
