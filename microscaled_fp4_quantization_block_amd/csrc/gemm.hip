@@ -42,7 +42,7 @@
 // - bf16 output (N % 8 == 0) leaves through LDS: the accumulators are written as bf16 into
 //   the drained code buffers (16-byte chunks XOR-swizzled by row), then every wave stores
 //   two full 512-byte tile rows per instruction, instead of 8 bytes per lane scattered
-//   over 32 rows.
+//   over 32 rows.  C stores are non-temporal.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,6 +89,13 @@ __device__ __forceinline__ Tile tile_of(int id, int tiles_m, int tiles_n) {
   t.m0 = (first_m + r % gm) * BM;
   t.n0 = (r / gm) * BN;
   return t;
+}
+
+// C is written once and never read back by this kernel: non-temporal stores keep it from
+// displacing operand panels in L2.
+template <typename V>
+__device__ __forceinline__ void store_streaming(void* p, V v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
 }
 
 // LDS slot of 16-byte chunk c of code row r: c ^ ((r / 2) % 8).  A 16-byte LDS read
@@ -399,7 +406,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
       const int m = (tid >> 5) + 2 * NW * k;
       const uint4 v = *reinterpret_cast<const uint4*>(ct + m * 512 + ((c ^ (m & 15)) << 4));
       const int gm = tile.m0 + m, gn = tile.n0 + 8 * c;
-      if (gm < M && gn < N) *reinterpret_cast<uint4*>(C16 + (int64_t)gm * N + gn) = v;
+      if (gm < M && gn < N) store_streaming(C16 + (int64_t)gm * N + gn, u32x4{v.x, v.y, v.z, v.w});
     }
     return;
   }
@@ -418,7 +425,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
         if (ctype == fp4impl::DT_BF16) {
           uint16_t* cp = reinterpret_cast<uint16_t*>(C) + (int64_t)m * N + n0;
           if (vec_ok && n0 + 3 < N) {
-            *reinterpret_cast<uint2*>(cp) = make_uint2(fp4dev::pack_bf16x2(c0, c1), fp4dev::pack_bf16x2(c2, c3));
+            store_streaming(cp, u32x2{fp4dev::pack_bf16x2(c0, c1), fp4dev::pack_bf16x2(c2, c3)});
           } else {
             if (n0 < N) cp[0] = (uint16_t)fp4dev::bf16_bits_rne(c0);
             if (n0 + 1 < N) cp[1] = (uint16_t)fp4dev::bf16_bits_rne(c1);
@@ -428,7 +435,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
         } else {
           float* cp = reinterpret_cast<float*>(C) + (int64_t)m * N + n0;
           if (vec_ok && n0 + 3 < N) {
-            *reinterpret_cast<float4*>(cp) = make_float4(c0, c1, c2, c3);
+            store_streaming(cp, u32x4{__float_as_uint(c0), __float_as_uint(c1), __float_as_uint(c2), __float_as_uint(c3)});
           } else {
             if (n0 < N) cp[0] = c0;
             if (n0 + 1 < N) cp[1] = c1;
