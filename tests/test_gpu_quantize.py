@@ -217,6 +217,36 @@ def test_dequantize_every_variant(fmt, h, out):
         P.assert_bf16_close(got, want, h, what="dequantized + inverse H, bf16")
 
 
+@pytest.mark.parametrize("fmt,h", [("mxfp4", 32), ("mxfp4", 16), ("nvfp4", 16), ("nvfp4", 32)])
+def test_rotated_fp32_input(fmt, h):
+    """fp32 input (not only bf16) through the rotated quantizers: rotated values, scales
+    and codes against the oracle under the boundary rule."""
+    _log(f"{fmt} H{h} fp32 input")
+    rng = np.random.default_rng(200 + h)
+    x = rng.standard_normal((29, 192)).astype(np.float32)
+    x[:, 11] *= 25
+    xg = torch.from_numpy(x).to(DEV)
+    xv = x.astype(np.float64)
+    dbg = torch.empty(x.shape, dtype=torch.float32, device=DEV)
+    codes, scales, ts = fp4.fp4_quantize(xg, fmt, h, dbg_rotated=dbg)
+    gc, gs = F.unpack_nibbles(_np(codes)), _np(scales)
+    if fmt == "mxfp4":
+        ref = mxfp4.quantize(xv, hadamard=h)
+        P.assert_values_close(_np(dbg), ref["y"], 32, what="rotated values")
+        P.check_e8m0_scales(gs, ref["scales"], ref["amax"])
+        c = mxfp4.quantize(xv, hadamard=h, block_scales=gs)
+        P.check_e2m1_codes(gc, c["codes"], c["elem_arg"], c["y"], 32)
+    else:
+        ref = nvfp4.quantize(xv, hadamard=h)
+        P.assert_values_close(_np(dbg), ref["y"], h, what="rotated values")
+        gst = _np(ts)[0]
+        P.assert_rel(gst, ref["tensor_scale"], what="tensor scale")
+        c1 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst)
+        P.check_e4m3_scales(gs, c1["scales"], c1["scale_arg"])
+        c2 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst, block_scales=gs)
+        P.check_e2m1_codes(gc, c2["codes"], c2["elem_arg"], c2["y"], 16)
+
+
 # ----------------------------------------------------------------------------- robustness
 
 def test_determinism_and_poisoned_outputs():
