@@ -33,6 +33,7 @@ namespace {
 constexpr int kMaxWaves = 8;
 constexpr int kLdsLimit = 144 * 1024;       // dynamic LDS per workgroup used here
 constexpr int kUnroll = 8;          // 16-byte loads in flight per lane
+constexpr int kStage = 8;           // permutation entries per thread staged in one batch
 #ifndef ARC_PIPE_WAVES
 #define ARC_PIPE_WAVES 8
 #endif
@@ -62,6 +63,19 @@ __device__ __forceinline__ void load_units(const uint16_t* __restrict__ xr, int 
   for (int i = 0; i < kUnroll; ++i) {
     const int u = u0 + 64 * i + lane;
     raw[i] = u < units ? reinterpret_cast<const uint4*>(xr)[u] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// The same chunk of a row of at most 64 kUnroll units, through a buffer resource over its
+// `units` 16-byte units: units past the end read as zero without a branch, so the loads
+// are straight-line code and a later wait can count them exactly.
+__device__ __forceinline__ void load_units_rsrc(const uint16_t* xr, int units, int lane, uint4 (&raw)[kUnroll]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xr), (short)0, units * 16, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (64 * i + lane) * 16, 0, 0);
+    raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -267,13 +281,30 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   const int64_t stride = (int64_t)gridDim.x * W;
   int64_t r = (int64_t)blockIdx.x * W + wave;
   const bool pipelined = units <= 64 * kUnroll;
-  // the first row's loads go out before the permutation is staged, so both are in flight
+  // An index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced.
   uint4 raw[kUnroll];
-  if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
-
-  // an index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced
-  for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
-  __syncthreads();
+  if (pipelined && K <= kStage * (int)blockDim.x) {
+    // The permutation's loads (L2-resident after the first workgroups) go out first, then
+    // the first row's.  The permutation is written to LDS as soon as its own loads land and
+    // the barrier waits for those LDS writes only, so the row stays in flight meanwhile.
+    // Indices are clamped so that every load is issued (a row past M reloads row M - 1,
+    // which is then never used).
+    uint32_t pv[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) pv[i] = (uint32_t)perm[min((int)threadIdx.x + i * (int)blockDim.x, K - 1)];
+    load_units_rsrc(x + (r < M ? r : M - 1) * K, units, lane, raw);   // pipelined: one chunk
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int c = threadIdx.x + i * blockDim.x;
+      if (c < K) ps[c] = (uint16_t)min(pv[i], (uint32_t)(K - 1));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt left open
+    __builtin_amdgcn_s_barrier();
+  } else {
+    if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
+    for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
+    __syncthreads();
+  }
 
   const float s_t = FMT == fp4impl::FMT_NV ? *tensor_scale : 0.0f;
   auto encode = [&](int64_t row, float inv_rms) {
