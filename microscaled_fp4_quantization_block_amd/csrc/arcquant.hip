@@ -113,13 +113,18 @@ __device__ __forceinline__ float inv_rms_of(float ss, int K, float eps) {
   return 1.0f / sqrtf(ss / (float)K + eps);
 }
 
-// z = fl(x / rms) (times gamma[c] when given): the normalised value of channel c.
-__device__ __forceinline__ float norm_value(uint16_t xb, float inv_rms, const float* __restrict__ gamma, int c) {
+// z = fl(x / rms), times the channel's gamma value g when the norm has a gain (kGamma):
+// the normalised value of one channel.  Whether a gain is present is a template
+// parameter, so the per-element path has no branch and the gains of a block are loaded
+// together before use.
+template <bool kGamma>
+__device__ __forceinline__ float norm_value(uint16_t xb, float inv_rms, float g) {
   const float y = __uint_as_float((uint32_t)xb << 16) * inv_rms;
-  return gamma ? y * gamma[c] : y;
+  return kGamma ? y * g : y;
 }
 
 // Statistics pass: running max|z| over the rows this wave visits, one atomic per wave.
+template <bool kGamma>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
             float* tensor_scale) {
@@ -136,10 +141,13 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
     for (int u = lane; u < units; u += 64) {
       const uint4 w = reinterpret_cast<const uint4*>(xs)[u];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      float g[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k] = kGamma ? gamma[8 * u + k] : 1.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        tmax = fmaxf(tmax, fabsf(norm_value((uint16_t)ws[k], inv_rms, gamma, 8 * u + 2 * k)));
-        tmax = fmaxf(tmax, fabsf(norm_value((uint16_t)(ws[k] >> 16), inv_rms, gamma, 8 * u + 2 * k + 1)));
+        tmax = fmaxf(tmax, fabsf(norm_value<kGamma>((uint16_t)ws[k], inv_rms, g[2 * k])));
+        tmax = fmaxf(tmax, fabsf(norm_value<kGamma>((uint16_t)(ws[k] >> 16), inv_rms, g[2 * k + 1])));
       }
     }
     wave_lds_sync();
@@ -174,6 +182,7 @@ __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K,
 // kBlocks blocks per lane are gathered together (all their LDS reads in flight at once)
 // before any of them is encoded.
 constexpr int kBlocks = 1;
+template <bool kGamma>
 __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
                                            int lane, float inv_rms, const float* __restrict__ gamma, float s_t,
                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -207,12 +216,15 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
       if (b >= nblk) break;
       const uint32_t w[8] = {pw[j][0].x, pw[j][0].y, pw[j][0].z, pw[j][0].w,
                              pw[j][1].x, pw[j][1].y, pw[j][1].z, pw[j][1].w};
-      float z[16];
+      float g[16];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        z[2 * k] = norm_value(xv[j][2 * k], inv_rms, gamma, (int)(w[k] & 0xFFFFu));
-        z[2 * k + 1] = norm_value(xv[j][2 * k + 1], inv_rms, gamma, (int)(w[k] >> 16));
+        g[2 * k] = kGamma ? gamma[w[k] & 0xFFFFu] : 1.0f;
+        g[2 * k + 1] = kGamma ? gamma[w[k] >> 16] : 1.0f;
       }
+      float z[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) z[k] = norm_value<kGamma>(xv[j][k], inv_rms, g[k]);
       if (dbg) store_f32<16>(dbg + r * K + 16 * b, z);
       encode_block(z, b, K, nblk, sblk, s_t, crow, srow);
     }
@@ -223,6 +235,7 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
 // by the hardware convert (exact: power-of-two scale).  The residual z - V 2^(e-127) is
 // exact in binary32: z lies within a factor of two of its nearest grid point, or the
 // grid point is 0.  Lane l takes blocks l, l + 64, ...
+template <bool kGamma>
 __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
                                               int lane, float inv_rms, const float* __restrict__ gamma,
                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -235,17 +248,22 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
     uint4 pw4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pw4[q] = reinterpret_cast<const uint4*>(ps)[4 * b + q];
-    float z[32];
+    int c[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t w[4] = {pw4[q].x, pw4[q].y, pw4[q].z, pw4[q].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int c0 = (int)(w[k] & 0xFFFFu), c1 = (int)(w[k] >> 16);
-        z[8 * q + 2 * k] = norm_value(xs[c0], inv_rms, gamma, c0);
-        z[8 * q + 2 * k + 1] = norm_value(xs[c1], inv_rms, gamma, c1);
+        c[8 * q + 2 * k] = (int)(w[k] & 0xFFFFu);
+        c[8 * q + 2 * k + 1] = (int)(w[k] >> 16);
       }
     }
+    float g[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gamma[c[k]] : 1.0f;
+    float z[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) z[k] = norm_value<kGamma>(xs[c[k]], inv_rms, g[k]);
     if (dbg) store_f32<32>(dbg + r * K + 32 * b, z);
     const uint32_t e = e8m0_from_amax(absmax<32>(z));
     const float sc = e8m0_value(e);
@@ -266,7 +284,7 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
   }
 }
 
-template <int FMT>
+template <int FMT, bool kGamma>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
            const int32_t* __restrict__ perm, int S, uint8_t* __restrict__ codes,
@@ -309,9 +327,9 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   const float s_t = FMT == fp4impl::FMT_NV ? *tensor_scale : 0.0f;
   auto encode = [&](int64_t row, float inv_rms) {
     if constexpr (FMT == fp4impl::FMT_NV)
-      encode_row(xs, ps, row, K, S, lane, inv_rms, gamma, s_t, codes, scales, dbg);
+      encode_row<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, s_t, codes, scales, dbg);
     else
-      encode_row_mx(xs, ps, row, K, S, lane, inv_rms, gamma, codes, scales, dbg);
+      encode_row_mx<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, codes, scales, dbg);
   };
   if (pipelined) {
     // whole row in one chunk: the next row's loads are in flight while this row is encoded
@@ -363,6 +381,27 @@ ArcLaunch arc_launch(int64_t M, int64_t K) {
   return a;
 }
 
+// Enqueue the statistics pass (when `compute`) and the quantizing kernel of format FMT,
+// with or without a gain vector.
+template <int FMT, bool kGamma>
+hipError_t launch_arc(const uint16_t* x, int64_t M, int64_t K, const float* gamma, float eps, const int32_t* perm,
+                      int64_t S, uint8_t* codes, uint8_t* scales, float* ts, bool compute, float* dbg,
+                      hipStream_t st) {
+  const ArcLaunch a = arc_launch(M, K);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT, kGamma>), a.lds_quant);
+  if (e == hipSuccess && compute) e = allow_lds(reinterpret_cast<const void*>(k_arc_stats<kGamma>), a.lds_stats);
+  if (e != hipSuccess) return e;
+  if (compute) {
+    k_zero_scalar<<<1, 1, 0, st>>>(ts);
+    if (M) k_arc_stats<kGamma><<<a.grid, 64 * a.W, a.lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
+    k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
+  }
+  if (M)
+    k_arcquant<FMT, kGamma><<<a.grid_q, 64 * a.Wq, a.lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S,
+                                                                     codes, scales, ts, dbg);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 namespace fp4impl {
@@ -371,31 +410,16 @@ hipError_t launch_residual_quantize(const uint16_t* x, int64_t M, int64_t K, con
                                     float eps, const int32_t* perm, int64_t S, uint8_t* codes,
                                     uint8_t* scales, float* ts, bool compute, float* dbg,
                                     hipStream_t st) {
-  const ArcLaunch a = arc_launch(M, K);
-  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arc_stats), a.lds_stats);
-  if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT_NV>), a.lds_quant);
-  if (e != hipSuccess) return e;
-  if (compute) {
-    k_zero_scalar<<<1, 1, 0, st>>>(ts);
-    if (M) k_arc_stats<<<a.grid, 64 * a.W, a.lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
-    k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
-  }
-  if (M)
-    k_arcquant<FMT_NV><<<a.grid_q, 64 * a.Wq, a.lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes,
-                                                               scales, ts, dbg);
-  return hipGetLastError();
+  return gamma ? launch_arc<FMT_NV, true>(x, M, K, gamma, eps, perm, S, codes, scales, ts, compute, dbg, st)
+               : launch_arc<FMT_NV, false>(x, M, K, gamma, eps, perm, S, codes, scales, ts, compute, dbg, st);
 }
 
 hipError_t launch_residual_quantize_mx(const uint16_t* x, int64_t M, int64_t K, const float* gamma, float eps,
                                        const int32_t* perm, int64_t S, uint8_t* codes, uint8_t* scales,
                                        float* dbg, hipStream_t st) {
   if (!M) return hipSuccess;
-  const ArcLaunch a = arc_launch(M, K);
-  hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT_MX>), a.lds_quant);
-  if (e != hipSuccess) return e;
-  k_arcquant<FMT_MX><<<a.grid_q, 64 * a.Wq, a.lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S, codes,
-                                                             scales, nullptr, dbg);
-  return hipGetLastError();
+  return gamma ? launch_arc<FMT_MX, true>(x, M, K, gamma, eps, perm, S, codes, scales, nullptr, false, dbg, st)
+               : launch_arc<FMT_MX, false>(x, M, K, gamma, eps, perm, S, codes, scales, nullptr, false, dbg, st);
 }
 
 }  // namespace fp4impl
