@@ -15,7 +15,8 @@
 //      wave's own LDS slice.
 //   2. A butterfly sum gives every lane the same sum, hence the same 1/rms.
 //   3. Lane l then encodes blocks l, l + 64, ...: the 16 channel indices of a block come
-//      from the permutation, staged once per workgroup in LDS as 16-bit indices, and the
+//      from the permutation, staged once per workgroup in LDS as 16-bit byte offsets into the
+//      row (2 c, below 2^15 for K <= 16384; one SDWA add forms each address), and the
 //      16 values are gathered from the LDS row.  Codes leave as 8-byte stores (512
 //      contiguous bytes per wave instruction), block scales as bytes (64 contiguous).
 //      Lanes whose block lies in the first S channels also encode the residual
@@ -178,6 +179,34 @@ __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K,
   }
 }
 
+// encode_block for z = fl(x inv_rms) without forming z on the primary path (no gain
+// vector).  The block maximum is max|x| times inv_rms, which equals the maximum of the
+// rounded products since rounding is monotone, so the block scale is the same as
+// encode_block's.  The elements are encoded as x fl(inv_rms / (s_b s_t)) instead of
+// fl(x inv_rms) / (s_b s_t): the product rounds once less, which moves an element's code
+// only when its quotient lies within a few ulp of a rounding boundary.  The residual
+// lanes form z as encode_block does.
+__device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], float inv_rms, int b, int K, int nblk,
+                                                      int sblk, float s_t, uint8_t* __restrict__ crow,
+                                                      uint8_t* __restrict__ srow) {
+  const float inv6s = recip_fast(6.0f * s_t);
+  const uint32_t sb = nvfp4_block_scale_fast(absmax<16>(x) * inv_rms, inv6s);
+  const float sbv = e4m3_value(sb);
+  const uint2 w = nvfp4_encode16_fast(x, inv_rms * recip_fast(sbv * s_t));
+  *reinterpret_cast<uint2*>(crow + 8 * b) = w;
+  srow[b] = (uint8_t)sb;
+  if (b < sblk) {
+    float q[16];
+    e2m1_decode8(w.x, 1.0f, q);
+    e2m1_decode8(w.y, 1.0f, q + 8);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, x[i] * inv_rms);   // z - V s_b s_t
+    const uint32_t sr = nvfp4_block_scale_fast(absmax<16>(q), inv6s);
+    *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t));
+    srow[nblk + b] = (uint8_t)sr;
+  }
+}
+
 // Gather, normalise and encode row r from its LDS copy: lane l takes blocks l + 64 j.
 // kBlocks blocks per lane are gathered together (all their LDS reads in flight at once)
 // before any of them is encoded.
@@ -206,8 +235,8 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
                              pw[j][1].x, pw[j][1].y, pw[j][1].z, pw[j][1].w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        xv[j][2 * k] = xs[w[k] & 0xFFFFu];
-        xv[j][2 * k + 1] = xs[w[k] >> 16];
+        xv[j][2 * k] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(xs) + (w[k] & 0xFFFFu));
+        xv[j][2 * k + 1] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(xs) + (w[k] >> 16));
       }
     }
 #pragma unroll
@@ -216,17 +245,30 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
       if (b >= nblk) break;
       const uint32_t w[8] = {pw[j][0].x, pw[j][0].y, pw[j][0].z, pw[j][0].w,
                              pw[j][1].x, pw[j][1].y, pw[j][1].z, pw[j][1].w};
-      float g[16];
+      if constexpr (kGamma) {
+        float g[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        g[2 * k] = kGamma ? gamma[w[k] & 0xFFFFu] : 1.0f;
-        g[2 * k + 1] = kGamma ? gamma[w[k] >> 16] : 1.0f;
+        for (int k = 0; k < 8; ++k) {
+          g[2 * k] = gamma[(w[k] & 0xFFFFu) >> 1];
+          g[2 * k + 1] = gamma[w[k] >> 17];
+        }
+        float z[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) z[k] = norm_value<true>(xv[j][k], inv_rms, g[k]);
+        if (dbg) store_f32<16>(dbg + r * K + 16 * b, z);
+        encode_block(z, b, K, nblk, sblk, s_t, crow, srow);
+      } else {
+        float xf[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) xf[k] = __uint_as_float((uint32_t)xv[j][k] << 16);
+        if (dbg) {
+          float z[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) z[k] = xf[k] * inv_rms;
+          store_f32<16>(dbg + r * K + 16 * b, z);
+        }
+        encode_block_unnormed(xf, inv_rms, b, K, nblk, sblk, s_t, crow, srow);
       }
-      float z[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) z[k] = norm_value<kGamma>(xv[j][k], inv_rms, g[k]);
-      if (dbg) store_f32<16>(dbg + r * K + 16 * b, z);
-      encode_block(z, b, K, nblk, sblk, s_t, crow, srow);
     }
   }
 }
@@ -254,16 +296,17 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
       const uint32_t w[4] = {pw4[q].x, pw4[q].y, pw4[q].z, pw4[q].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        c[8 * q + 2 * k] = (int)(w[k] & 0xFFFFu);
+        c[8 * q + 2 * k] = (int)(w[k] & 0xFFFFu);         // byte offsets
         c[8 * q + 2 * k + 1] = (int)(w[k] >> 16);
       }
     }
     float g[32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gamma[c[k]] : 1.0f;
+    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gamma[c[k] >> 1] : 1.0f;
     float z[32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) z[k] = norm_value<kGamma>(xs[c[k]], inv_rms, g[k]);
+    for (int k = 0; k < 32; ++k)
+      z[k] = norm_value<kGamma>(*reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(xs) + c[k]), inv_rms, g[k]);
     if (dbg) store_f32<32>(dbg + r * K + 32 * b, z);
     const uint32_t e = e8m0_from_amax(absmax<32>(z));
     const float sc = e8m0_value(e);
@@ -292,7 +335,7 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  uint16_t* ps = smem;                                   // [K] permutation (16-bit)
+  uint16_t* ps = smem;                                   // [K] permutation, as byte offsets 2 perm[c]
   uint16_t* xs = smem + (size_t)(1 + wave) * K;          // [K] this wave's row
 
   const int units = K / 8;
@@ -314,13 +357,13 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
       const int c = threadIdx.x + i * blockDim.x;
-      if (c < K) ps[c] = (uint16_t)min(pv[i], (uint32_t)(K - 1));
+      if (c < K) ps[c] = (uint16_t)(2 * min(pv[i], (uint32_t)(K - 1)));
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt left open
     __builtin_amdgcn_s_barrier();
   } else {
     if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
-    for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)min((uint32_t)perm[c], (uint32_t)(K - 1));
+    for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)(2 * min((uint32_t)perm[c], (uint32_t)(K - 1)));
     __syncthreads();
   }
 
