@@ -284,22 +284,10 @@ __device__ __forceinline__ float e8m0_value(uint32_t code) {
 
 constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]: value of lane ^ 1
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]: value of lane ^ 2
-constexpr int kQuadRev = 0x1B;    // quad_perm [3,2,1,0]: value of lane ^ 3
-constexpr int kRowHalfMirror = 0x141;   // value of lane ^ 7 within 8 lanes
-constexpr int kRowMirror = 0x140;       // value of lane ^ 15 within 16 lanes
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Value held by lane ^ X (X = 1, 2, 4 or 8; 4 and 8 compose two row permutations).
-template <int X>
-__device__ __forceinline__ float lane_xor(float v) {
-  if constexpr (X == 1) return dpp_move<kQuadXor1>(v);
-  else if constexpr (X == 2) return dpp_move<kQuadXor2>(v);
-  else if constexpr (X == 4) return dpp_move<kQuadRev>(dpp_move<kRowHalfMirror>(v));   // (i ^ 7) ^ 3
-  else return dpp_move<kRowHalfMirror>(dpp_move<kRowMirror>(v));                     // (i ^ 15) ^ 7
 }
 
 template <int CTRL>
@@ -307,13 +295,71 @@ __device__ __forceinline__ float quad_partner(float v) {
   return dpp_move<CTRL>(v);
 }
 
-// One Walsh-Hadamard butterfly across lane pairs: the lower lane (bit clear) keeps
-// own + partner, the upper one partner - own, i.e. (a + b, a - b) exactly as the in-lane
-// butterfly computes them (fma with -1 is an exact negation inside one rounding).
+// Walsh-Hadamard butterflies across lane pairs, in signed form: every lane computes
+// own + s partner with s = +1 on the lower lane of the pair (bit clear) and -1 on the upper
+// one.  The lower lane gets a + b as the in-lane butterfly does; the upper lane gets
+// b - a = -(a - b), the butterfly's output negated.  Negation commutes with rounding, so
+// after several stages a lane holds its true value times the product of its stage signs,
+// and the caller folds that sign into the final normalisation: every nonzero result is
+// bit for bit the plain butterflies' result.  An exact zero is the one exception: an
+// exactly cancelling sum rounds to +0 whatever the lane's sign, so after the fold it can
+// come out as -0 where the plain butterflies give +0 (equal as numbers).
+//
+// Eight signed butterflies across lane pairs ^X at once: v[j] += v[j](lane ^ X) * s, as
+// v_fmac_f32 with a DPP source (the compiler keeps the DPP move separate).  X = 1, 2 read
+// the partner through one quad permutation; X = 4, 8 first move v[j] through a row
+// mirror into a temporary and read the temporary through a second permutation (4: half
+// mirror then quad reverse, (i ^ 7) ^ 3; 8: mirror then half mirror, (i ^ 15) ^ 7).  The
+// leading s_nop 1 provides the two wait states a DPP read needs after a VALU write of its
+// source; inside the block every DPP source was written at least eight instructions
+// earlier.  Each fma rounds once: own + s partner exactly, then one rounding.
+#define FP4_FMAC8(CTRL, S0, S1, S2, S3, S4, S5, S6, S7)                                       \
+  "v_fmac_f32_dpp %0, " S0 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %1, " S1 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %2, " S2 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %3, " S3 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %4, " S4 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %5, " S5 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %6, " S6 ", %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+  "v_fmac_f32_dpp %7, " S7 ", %16 " CTRL " row_mask:0xf bank_mask:0xf"
+#define FP4_MOV8(CTRL)                                                                      \
+  "v_mov_b32_dpp %8, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                            \
+  "v_mov_b32_dpp %9, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                            \
+  "v_mov_b32_dpp %10, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_mov_b32_dpp %11, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_mov_b32_dpp %12, %4 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_mov_b32_dpp %13, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_mov_b32_dpp %14, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_mov_b32_dpp %15, %7 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+
 template <int X>
-__device__ __forceinline__ float lane_butterfly(float own, float sign) {
-  return fmaf(own, sign, lane_xor<X>(own));
+__device__ __forceinline__ void lane_butterflies8_signed(float* v, float s) {
+  float t[8];
+#define FP4_OPERANDS                                                                        \
+  : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),    \
+    "+v"(v[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]),           \
+    "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])                                                    \
+  : "v"(s)
+  if constexpr (X == 1) {
+    asm volatile("s_nop 1\n\t" FP4_FMAC8("quad_perm:[1,0,3,2]", "%0", "%1", "%2", "%3", "%4", "%5", "%6", "%7")
+                 FP4_OPERANDS);
+  } else if constexpr (X == 2) {
+    asm volatile("s_nop 1\n\t" FP4_FMAC8("quad_perm:[2,3,0,1]", "%0", "%1", "%2", "%3", "%4", "%5", "%6", "%7")
+                 FP4_OPERANDS);
+  } else if constexpr (X == 4) {
+    asm volatile("s_nop 1\n\t" FP4_MOV8("row_half_mirror")
+                 FP4_FMAC8("quad_perm:[3,2,1,0]", "%8", "%9", "%10", "%11", "%12", "%13", "%14", "%15")
+                 FP4_OPERANDS);
+  } else {
+    static_assert(X == 8, "lane distance 1, 2, 4 or 8");
+    asm volatile("s_nop 1\n\t" FP4_MOV8("row_mirror")
+                 FP4_FMAC8("row_half_mirror", "%8", "%9", "%10", "%11", "%12", "%13", "%14", "%15")
+                 FP4_OPERANDS);
+  }
+#undef FP4_OPERANDS
 }
+#undef FP4_FMAC8
+#undef FP4_MOV8
 
 // Orthonormal H_B over a block spread as 8 contiguous elements per lane across B / 8
 // consecutive lanes of a quad (lane p = position within the quad): the in-lane stages
@@ -324,15 +370,15 @@ __device__ __forceinline__ void quad_hadamard8(float (&v)[8], int p) {
   if constexpr (B >= 16) {
     fwht_inplace<8>(v);
     const float s1 = (p & 1) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<1>(v[j], s1);
+    lane_butterflies8_signed<1>(v, s1);
+    float norm = s1 * InvSqrt<B>::v;
     if constexpr (B == 32) {
       const float s2 = (p & 2) ? -1.0f : 1.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<2>(v[j], s2);
+      lane_butterflies8_signed<2>(v, s2);
+      norm *= s2;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] *= InvSqrt<B>::v;
+    for (int j = 0; j < 8; ++j) v[j] *= norm;
   }
 }
 
@@ -345,16 +391,13 @@ __device__ __forceinline__ void group16_two_level_fwht8(float (&v)[8], int g) {
   fwht_inplace<8>(v);
   const float s1 = (g & 1) ? -1.0f : 1.0f, s2 = (g & 2) ? -1.0f : 1.0f;
   const float s4 = (g & 4) ? -1.0f : 1.0f, s8 = (g & 8) ? -1.0f : 1.0f;
+  lane_butterflies8_signed<1>(v, s1);
+  lane_butterflies8_signed<2>(v, s2);
+  lane_butterflies8_signed<4>(v, s4);
+  lane_butterflies8_signed<8>(v, s8);
+  const float norm = (__popc(g & 15) & 1) ? -InvSqrt<128>::v : InvSqrt<128>::v;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<1>(v[j], s1);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<2>(v[j], s2);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<4>(v[j], s4);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = lane_butterfly<8>(v[j], s8);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] *= InvSqrt<128>::v;
+  for (int j = 0; j < 8; ++j) v[j] *= norm;
 }
 
 // --------------------------------------------------------------------------- reductions

@@ -40,9 +40,9 @@ __device__ __forceinline__ void quad_two_level_fwht(float* v, int p) {
   const float c1 = (p & 1) ? -1.0f : 1.0f;
   const float c2 = (p & 2) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = fmaf(quad_partner<kQuadXor1>(v[i]), c1, v[i]);
+  for (int q = 0; q < 4; ++q) lane_butterflies8_signed<1>(v + 8 * q, c1);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = fmaf(quad_partner<kQuadXor2>(v[i]), c2, v[i]);
+  for (int q = 0; q < 4; ++q) lane_butterflies8_signed<2>(v + 8 * q, c2);
   const float norm = (__popc(p) & 1) ? -InvSqrt<128>::v : InvSqrt<128>::v;
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] *= norm;
