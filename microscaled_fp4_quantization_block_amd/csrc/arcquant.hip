@@ -157,6 +157,80 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
   if (lane == 0 && tmax > 0.0f) atomic_max_nonneg(tensor_scale, tmax);
 }
 
+// Statistics pass for rows of at most 64 kUnroll units: rows stay in registers (no LDS
+// copy), two per wave per step with both rows' loads in flight.  The sum of squares takes
+// the same per-lane order as park_units and the same butterfly, so 1/rms is the
+// quantizing pass's to the bit.  Without a gain vector the row's max|z| is max|x| times
+// 1/rms, which by monotone rounding equals the maximum of the rounded products; with one,
+// every element's fl(fl(x / rms) g) is formed as norm_value does.  The maximum is reduced
+// over the workgroup before its single atomic: atomics on one address serialise, so the
+// grid is kept to at most kStatsGroups workgroups.
+constexpr int kStatsGroups = 256;
+
+template <bool kGamma>
+__device__ __forceinline__ float row_absmax(const uint4 (&raw)[kUnroll], int units, int lane, int K, float eps,
+                                            const float* __restrict__ gamma) {
+  float ss = 0.0f, am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float a = bf16_lo(w[k]), b = bf16_hi(w[k]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+      am = fmaxf(am, fmaxf(fabsf(a), fabsf(b)));
+    }
+  }
+  const float inv_rms = inv_rms_of(wave_sum(ss), K, eps);
+  if constexpr (!kGamma) return am * inv_rms;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const int u = 64 * i + lane;
+    if (u < units) {
+      float g[8];                                          // gamma is only 4-byte aligned
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k] = gamma[8 * u + k];
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        m = fmaxf(m, fabsf(norm_value<true>((uint16_t)w[k], inv_rms, g[2 * k])));
+        m = fmaxf(m, fabsf(norm_value<true>((uint16_t)(w[k] >> 16), inv_rms, g[2 * k + 1])));
+      }
+    }
+  }
+  return m;
+}
+
+template <bool kGamma>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+k_arc_stats_rows(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
+                 float* tensor_scale) {
+  __shared__ float wmax[kMaxWaves];
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int units = K / 8;
+  const int64_t stride = (int64_t)gridDim.x * W;
+  float tmax = 0.0f;
+  for (int64_t r = (int64_t)blockIdx.x * W + wave; r < M; r += 2 * stride) {
+    const int64_t r2 = r + stride < M ? r + stride : r;   // a missing second row repeats the first
+    uint4 a[kUnroll], b[kUnroll];
+    load_units_rsrc(x + r * K, units, lane, a);
+    load_units_rsrc(x + r2 * K, units, lane, b);
+    tmax = fmaxf(tmax, row_absmax<kGamma>(a, units, lane, K, eps, gamma));
+    tmax = fmaxf(tmax, row_absmax<kGamma>(b, units, lane, K, eps, gamma));
+  }
+  tmax = wave_max(tmax);
+  if (lane == 0) wmax[wave] = tmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.0f;
+    for (int w = 0; w < W; ++w) m = fmaxf(m, wmax[w]);
+    if (m > 0.0f) atomic_max_nonneg(tensor_scale, m);
+  }
+}
+
 // Encode one 16-channel block: primary NVFP4 codes and scale, and for blocks inside the
 // first S channels the residual z - V s_b s_t and its codes and scale.
 __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K, int nblk, int sblk, float s_t,
@@ -432,11 +506,18 @@ hipError_t launch_arc(const uint16_t* x, int64_t M, int64_t K, const float* gamm
                       hipStream_t st) {
   const ArcLaunch a = arc_launch(M, K);
   hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT, kGamma>), a.lds_quant);
-  if (e == hipSuccess && compute) e = allow_lds(reinterpret_cast<const void*>(k_arc_stats<kGamma>), a.lds_stats);
+  if (e == hipSuccess && compute && K / 8 > 64 * kUnroll)
+    e = allow_lds(reinterpret_cast<const void*>(k_arc_stats<kGamma>), a.lds_stats);
   if (e != hipSuccess) return e;
   if (compute) {
     k_zero_scalar<<<1, 1, 0, st>>>(ts);
-    if (M) k_arc_stats<kGamma><<<a.grid, 64 * a.W, a.lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
+    if (M && K / 8 <= 64 * kUnroll) {
+      const int64_t wg = (M + 2 * kMaxWaves - 1) / (2 * kMaxWaves);   // two rows per wave per step
+      k_arc_stats_rows<kGamma><<<(unsigned)(wg < kStatsGroups ? wg : kStatsGroups), 64 * kMaxWaves, 0, st>>>(
+          x, M, (int)K, gamma, eps, ts);
+    } else if (M) {
+      k_arc_stats<kGamma><<<a.grid, 64 * a.W, a.lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
+    }
     k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
   if (M)

@@ -99,3 +99,29 @@ def test_arcquant_multi_row_and_long_rows(M, K, S, gam):
     gamma = rng.uniform(0.5, 1.5, K) if gam else None
     rows = np.unique(np.concatenate([W.seeded_rows(M, min(M, 48), 9), [0, M - 1]]))
     _check_arc(xt, perm, S, gamma=gamma, rows=rows)
+
+
+@pytest.mark.parametrize("M,K,gam", [(1, 256, False), (300, 1024, True), (4099, 512, False), (77, 4096, True),
+                                     (5, 8192, False)])
+def test_dynamic_scale_matches_quantizing_pass(M, K, gam):
+    """The statistics pass and the quantizing pass form the same binary32 z: the computed
+    tensor scale is exactly fl32(max |z| / 2688) over the quantizing pass's own normalised
+    values (dbg_normed), and the whole result passes the oracle parity checks.  Covers the
+    register-resident statistics pass (rows up to 4096 channels, one or two rows per wave
+    step, with and without a gain vector) and the chunked pass for longer rows."""
+    print(f"arcquant dynamic scale M={M} K={K} gamma={gam}", flush=True)
+    rng = np.random.default_rng(M * 7 + K)
+    x = rng.standard_normal((M, K))
+    x[:, rng.choice(K, max(1, K // 64), replace=False)] *= 30
+    xt = W.to_bf16(x)
+    perm = rng.permutation(K).astype(np.int32)
+    gamma = rng.uniform(0.5, 1.5, K) if gam else None
+    g = None if gamma is None else torch.from_numpy(gamma.astype(np.float32)).to(DEV)
+    dbg = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    _, _, ts = fp4.fp4_residual_quantize(xt.to(DEV), torch.from_numpy(perm).to(DEV), 16, gamma=g,
+                                         tensor_scale=torch.zeros(1, dtype=torch.float32, device=DEV),
+                                         mode="compute", dbg_normed=dbg)
+    zmax = np.float32(np.max(np.abs(_np(dbg))))
+    assert _np(ts)[0] == zmax / np.float32(2688.0)
+    rows = np.unique(np.concatenate([W.seeded_rows(M, min(M, 24), 3), [0, M - 1]]))
+    _check_arc(xt, perm, 16, gamma=gamma, rows=rows)
