@@ -33,19 +33,27 @@ __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 // s_t = fl32(amax / 2688), in place (correctly rounded fp32 division).
 __global__ void k_finalize_tensor_scale(float* p) { *p = *p / kTensorDivisor; }
 
-// Per-tensor maximum of |H x| (running atomic max into *amax, which starts at 0).
+// Per-tensor maximum of |H x| (running atomic max into *amax, which starts at 0).  A
+// grid-stride walk over the chunks, reduced over the workgroup before its one atomic:
+// atomics on a single address serialise, so the grid is capped at kAmaxGroups.
+constexpr int kAmaxThreads = 1024, kAmaxGroups = 256;
 template <int DT, int H>
-__global__ void __launch_bounds__(kThreads) k_amax(const void* x, int64_t nchunks, float* amax) {
-  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void __launch_bounds__(kAmaxThreads) k_amax(const void* x, int64_t nchunks, float* amax) {
+  __shared__ float wm[kAmaxThreads / 64];
   float m = 0.0f;
-  if (c < nchunks) {
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
     float v[32];
     load_chunk<DT>(x, c, v);
     block_hadamard<32, H>(v);
-    m = absmax<32>(v);
+    m = fmaxf(m, absmax<32>(v));
   }
   m = wave_max(m);
-  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomic_max_nonneg(amax, m);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, wm[w]);
+    if (m > 0.0f) atomic_max_nonneg(amax, m);
+  }
 }
 
 template <int DT, int H>
@@ -155,7 +163,11 @@ hipError_t quantize_t(const void* x, int64_t nchunks, int fmt, uint8_t* codes, u
   }
   if (compute) {
     k_zero_scalar<<<1, 1, 0, st>>>(ts);
-    if (nchunks) k_amax<DT, H><<<g, b, 0, st>>>(x, nchunks, ts);
+    if (nchunks) {
+      const int64_t t = nchunks >= 65536 ? kAmaxThreads : kThreads;
+      const int64_t wg = (nchunks + t - 1) / t;
+      k_amax<DT, H><<<dim3((unsigned)(wg < kAmaxGroups ? wg : kAmaxGroups)), dim3((unsigned)t), 0, st>>>(x, nchunks, ts);
+    }
     k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
   if (nchunks) k_quant_nv<DT, H><<<g, b, 0, st>>>(x, nchunks, codes, scales, ts, dbg);

@@ -269,3 +269,29 @@ def test_canary_after_outputs():
     scales = sbuf[:M * K // 16].view(M, K // 16)
     fp4.fp4_quantize(x, "nvfp4", 0, codes=codes, scales=scales)
     assert (_np(buf)[M * K // 2:] == 0x5A).all() and (_np(sbuf)[M * K // 16:] == 0x5A).all()
+
+
+@pytest.mark.parametrize("h", [0, 16])
+def test_nvfp4_dynamic_scale_large_tensor(h):
+    """A tensor with more 32-element chunks than one pass of the maximum kernel's grid
+    (4097 x 4096 bf16: 524,416 chunks against 256 x 1024 threads), so every thread walks
+    several chunks and the workgroup maxima meet in one atomic each.  Unrotated, the scale
+    equals the oracle's fl32(max|x| / 2688) bit for bit and sampled rows are bit-exact;
+    rotated, it equals fl32(max|Hx| / 2688) over the kernel's own rotated values."""
+    _log(f"nvfp4 dynamic scale 4097x4096 H{h}")
+    rng = np.random.default_rng(4097 + h)
+    x = rng.standard_normal((4097, 4096)) * 2
+    x[rng.integers(0, 4097), rng.integers(0, 4096)] = 417.0          # a single tensor maximum
+    xt = W.to_bf16(x)
+    dbg = torch.empty((4097, 4096), dtype=torch.float32, device=DEV) if h else None
+    codes, scales, ts = fp4.fp4_quantize(xt.to(DEV), "nvfp4", h, dbg_rotated=dbg)
+    gst = _np(ts)[0]
+    rows = W.seeded_rows(4097, 12, 5)
+    if h == 0:
+        assert gst.tobytes() == np.float32(nvfp4.tensor_scale(_vals(xt))).tobytes()
+        ref = nvfp4.quantize(_vals(xt)[rows], tensor_scale_value=gst)
+        assert np.array_equal(_np(scales)[rows], ref["scales"])
+        assert np.array_equal(_np(codes)[rows], ref["packed"])
+    else:
+        zmax = np.float32(np.max(np.abs(_np(dbg))))
+        assert gst == zmax / np.float32(2688.0)
