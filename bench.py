@@ -72,10 +72,13 @@ class Timer:
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline_gemm(a_bf16, w_bf16, rows=8192, cols=16384):
-    """Oracle (float64 numpy) on a bounded sample of the step: Hadamard-32 MXFP4 of `rows`
-    activation rows, then their GEMM against `cols` weight rows quantized the same way
-    (untimed setup).  Throughput in the step's unit: 2 rows cols K / time."""
+def cpu_baseline_gemm(a_bf16, w_bf16, rows=None, cols=None):
+    """Oracle (float64 numpy) on a bounded sample of the step, by default all of it:
+    Hadamard-32 MXFP4 of `rows` activation rows, then their GEMM against `cols` weight rows
+    quantized the same way (untimed setup).  Throughput in the step's unit:
+    2 rows cols K / time."""
+    rows = a_bf16.shape[0] if rows is None else rows
+    cols = w_bf16.shape[0] if cols is None else cols
     from threadpoolctl import threadpool_info
     from oracle import gemm, mxfp4
     K = a_bf16.shape[1]
