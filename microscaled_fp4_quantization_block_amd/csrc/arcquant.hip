@@ -35,17 +35,14 @@ constexpr int kMaxWaves = 8;
 constexpr int kLdsLimit = 144 * 1024;       // dynamic LDS per workgroup used here
 constexpr int kUnroll = 8;          // 16-byte loads in flight per lane
 constexpr int kStage = 8;           // permutation entries per thread staged in one batch
-#ifndef ARC_PIPE_WAVES
-#define ARC_PIPE_WAVES 8
-#endif
-#ifndef ARC_PIPE_TOTAL
-#define ARC_PIPE_TOTAL 4096
-#endif
 // Rows of at most 64 kUnroll 16-byte units are software-pipelined: kPipeWaves waves per
 // workgroup and at most kPipeTotal waves in all (16 per CU), each walking several
 // rows with the next row's loads in flight.
-constexpr int kPipeWaves = ARC_PIPE_WAVES;
-constexpr int kPipeTotal = ARC_PIPE_TOTAL;
+constexpr int kPipeWaves = 8;
+constexpr int kPipeTotal = 4096;
+// Statistics passes end in one atomic maximum per workgroup; atomics on one address
+// serialise, so their grids are capped at kStatsGroups workgroups.
+constexpr int kStatsGroups = 256;
 
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 __global__ void k_finalize_tensor_scale(float* p) { *p = *p / 2688.0f; }
@@ -124,7 +121,21 @@ __device__ __forceinline__ float norm_value(uint16_t xb, float inv_rms, float g)
   return kGamma ? y * g : y;
 }
 
-// Statistics pass: running max|z| over the rows this wave visits, one atomic per wave.
+// Maximum of m over the workgroup, then one atomic max into *dst.  Every thread of the
+// workgroup calls it (it holds a barrier).
+__device__ __forceinline__ void workgroup_atomic_max(float m, float* dst) {
+  __shared__ float wmax[kMaxWaves];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, wmax[w]);
+    if (m > 0.0f) atomic_max_nonneg(dst, m);
+  }
+}
+
+// Statistics pass for rows of any length: each wave streams its rows through its LDS
+// slice in chunks, keeping a running max|z|.
 template <bool kGamma>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
@@ -153,8 +164,7 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
     }
     wave_lds_sync();
   }
-  tmax = wave_max(tmax);
-  if (lane == 0 && tmax > 0.0f) atomic_max_nonneg(tensor_scale, tmax);
+  workgroup_atomic_max(tmax, tensor_scale);
 }
 
 // Statistics pass for rows of at most 64 kUnroll units: rows stay in registers (no LDS
@@ -162,10 +172,7 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
 // the same per-lane order as park_units and the same butterfly, so 1/rms is the
 // quantizing pass's to the bit.  Without a gain vector the row's max|z| is max|x| times
 // 1/rms, which by monotone rounding equals the maximum of the rounded products; with one,
-// every element's fl(fl(x / rms) g) is formed as norm_value does.  The maximum is reduced
-// over the workgroup before its single atomic: atomics on one address serialise, so the
-// grid is kept to at most kStatsGroups workgroups.
-constexpr int kStatsGroups = 256;
+// every element's fl(fl(x / rms) g) is formed as norm_value does.
 
 template <bool kGamma>
 __device__ __forceinline__ float row_absmax(const uint4 (&raw)[kUnroll], int units, int lane, int K, float eps,
@@ -207,7 +214,6 @@ template <bool kGamma>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 k_arc_stats_rows(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
                  float* tensor_scale) {
-  __shared__ float wmax[kMaxWaves];
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int units = K / 8;
@@ -221,14 +227,7 @@ k_arc_stats_rows(const uint16_t* __restrict__ x, int64_t M, int K, const float* 
     tmax = fmaxf(tmax, row_absmax<kGamma>(a, units, lane, K, eps, gamma));
     tmax = fmaxf(tmax, row_absmax<kGamma>(b, units, lane, K, eps, gamma));
   }
-  tmax = wave_max(tmax);
-  if (lane == 0) wmax[wave] = tmax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float m = 0.0f;
-    for (int w = 0; w < W; ++w) m = fmaxf(m, wmax[w]);
-    if (m > 0.0f) atomic_max_nonneg(tensor_scale, m);
-  }
+  workgroup_atomic_max(tmax, tensor_scale);
 }
 
 // Encode one 16-channel block: primary NVFP4 codes and scale, and for blocks inside the
@@ -516,7 +515,8 @@ hipError_t launch_arc(const uint16_t* x, int64_t M, int64_t K, const float* gamm
       k_arc_stats_rows<kGamma><<<(unsigned)(wg < kStatsGroups ? wg : kStatsGroups), 64 * kMaxWaves, 0, st>>>(
           x, M, (int)K, gamma, eps, ts);
     } else if (M) {
-      k_arc_stats<kGamma><<<a.grid, 64 * a.W, a.lds_stats, st>>>(x, M, (int)K, gamma, eps, ts);
+      k_arc_stats<kGamma><<<a.grid < kStatsGroups ? a.grid : kStatsGroups, 64 * a.W, a.lds_stats, st>>>(
+          x, M, (int)K, gamma, eps, ts);
     }
     k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
