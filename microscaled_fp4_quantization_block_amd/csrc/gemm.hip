@@ -70,7 +70,6 @@ constexpr uint32_t kOOB = 0x80000000u;             // offset past every resource
 
 // Wave arrangement: NW waves as WM x WN, each owning TI x TJ MFMA blocks of 32 x 32.
 template <int NW> struct Cfg;
-template <> struct Cfg<4> { static constexpr int WM = 2, WN = 2, TI = 4, TJ = 4; };
 template <> struct Cfg<8> { static constexpr int WM = 4, WN = 2, TI = 2, TJ = 4; };
 
 struct Tile { int m0, n0; };
@@ -453,10 +452,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
 
 namespace fp4impl {
 
-#ifndef FP4_GEMM_WAVES
-#define FP4_GEMM_WAVES 8
-#endif
-constexpr int kWaves = FP4_GEMM_WAVES;
+constexpr int kWaves = 8;
 
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, void* c, int ctype, hipStream_t st) {
