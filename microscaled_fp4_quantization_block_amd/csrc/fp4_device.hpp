@@ -262,6 +262,44 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale_fast(float amax, float inv
   return e4m3_fast(amax * inv6s);
 }
 
+// Exact decisions without float64 in the common case.  The exact NVFP4 path needs
+// RNE_E4M3(amax / (6 s_t)) and RNE_E2M1(x / (s_b s_t)) of the real quotients.  In binary32,
+// q = a * fl32(rcp(fl32(d))) with d = 6 s_t or s_b s_t lies within 2^-22 (relative) of the
+// real quotient a / d, for d normal: one rounding of d (2^-24), the 1-ulp reciprocal
+// (2^-23), one rounding of the product (2^-24).  If q (1 - 2^-19) and q (1 + 2^-19), each
+// rounded once more, still round to the same code, the real quotient lies between them
+// and, the rounding being monotone, rounds to that code too.  Otherwise (a quotient
+// within about 2^-19 of a rounding boundary: ties, near-ties) the caller takes the
+// float64 decision.  A quotient below the binary32 normal range is far below the first
+// E2M1 / E4M3 boundary and needs no bound; a saturated one gives equal codes at both ends.
+constexpr float kBelow = 1.0f - 0x1p-19f, kAbove = 1.0f + 0x1p-19f;
+
+// A divisor d for which the bound above holds: normal and finite.
+__device__ __forceinline__ bool checked_divisor(float d) { return d >= 0x1p-126f && d <= 0x1p+126f; }
+
+// E4M3 code of amax * inv6s (inv6s = recip_fast(6 s_t)); false if it may differ from the
+// code of the real quotient.
+__device__ __forceinline__ bool nvfp4_block_scale_checked(float amax, float inv6s, uint32_t& code) {
+  const float r = amax * inv6s;
+  code = e4m3_fast(r);
+  return e4m3_fast(r * kBelow) == e4m3_fast(r * kAbove);
+}
+
+// E2M1 codes of v * E (E = recip_fast(s_b s_t)); false if any may differ from the code of
+// the real quotient.
+__device__ __forceinline__ bool nvfp4_encode16_checked(const float* v, float E, uint2& w) {
+  float q[16], lo[16], hi[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    q[i] = v[i] * E;
+    lo[i] = q[i] * kBelow;
+    hi[i] = q[i] * kAbove;
+  }
+  w = e2m1_encode16(q, 1.0f);
+  const uint2 a = e2m1_encode16(lo, 1.0f), b = e2m1_encode16(hi, 1.0f);
+  return a.x == b.x && a.y == b.y;
+}
+
 // --------------------------------------------------------------------------- E8M0
 
 // MX scale code of a block maximum: floor(log2 amax) - 2 + 127, clamped to [0, 254];

@@ -71,7 +71,8 @@ k_quant_mx(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales, floa
 }
 
 // NVFP4: two 16-blocks per chunk.  Unrotated input takes the exact scale and element
-// decisions (float64 quotients); rotated input (already fp32-rounded) the fast ones.
+// decisions (binary32 with a certified margin, float64 quotients where the margin is too
+// thin); rotated input (already fp32-rounded) the fast ones.
 template <int DT, int H>
 __global__ void __launch_bounds__(kThreads)
 k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
@@ -88,13 +89,19 @@ k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
   const float inv6s = recip_fast(6.0f * s_t);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    sb[b] = H == 0 ? nvfp4_block_scale(absmax<16>(v + 16 * b), s_t)
-                   : nvfp4_block_scale_fast(absmax<16>(v + 16 * b), inv6s);
     if constexpr (H == 0) {
-      double S = (double)e4m3_value(sb[b]) * (double)s_t;     // exact
-      double R = S > 0.0 ? 1.0 / S : 0.0;
-      w[b] = nvfp4_encode16_exact(v + 16 * b, R);
+      // Exact decisions: binary32 with a certified margin, float64 where it is too thin.
+      const float amax = absmax<16>(v + 16 * b);
+      bool ok = checked_divisor(6.0f * s_t) && nvfp4_block_scale_checked(amax, inv6s, sb[b]);
+      if (!ok) sb[b] = nvfp4_block_scale(amax, s_t);
+      const float S32 = e4m3_value(sb[b]) * s_t;
+      ok = checked_divisor(S32) && nvfp4_encode16_checked(v + 16 * b, recip_fast(S32), w[b]);
+      if (!ok) {
+        const double S = (double)e4m3_value(sb[b]) * (double)s_t;     // exact
+        w[b] = nvfp4_encode16_exact(v + 16 * b, S > 0.0 ? 1.0 / S : 0.0);
+      }
     } else {
+      sb[b] = nvfp4_block_scale_fast(absmax<16>(v + 16 * b), inv6s);
       w[b] = nvfp4_encode16_fast(v + 16 * b, recip_fast(e4m3_value(sb[b]) * s_t));
     }
   }
