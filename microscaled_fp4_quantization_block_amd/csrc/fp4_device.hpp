@@ -192,16 +192,18 @@ __device__ __forceinline__ float round_to_odd_f32(double q) {
   return __uint_as_float(f);
 }
 
-// Exact NVFP4 element codes of 16 values: RNE(|x| / S) with R = 1/S correctly rounded in
-// float64 (R = 0 when S = 0 gives sign-only codes).  A float64 product |x| R lies within
-// 2^-52 (relative) of the real quotient, every non-midpoint quotient is at least 2^-33
-// away from a midpoint, and a midpoint quotient is recovered exactly, so the decisions
-// equal those of the exact quotient.
-__device__ __forceinline__ uint2 nvfp4_encode16_exact(const float* v, double R) {
+// Exact NVFP4 element codes of 16 values: RNE(|x| / S) for S = s_b s_t (exact in
+// float64), sign kept; S = 0 gives sign-only codes.  Each quotient is a correctly rounded
+// float64 division: a quotient that is an E2M1 midpoint comes out as that midpoint exactly,
+// and any other lies at least 2^-31 (relative) from every midpoint (|x| has 24 significant
+// bits, the midpoint times S at most 31), far beyond the division's 2^-53.  A product with
+// a rounded reciprocal 1/S would not do: at a tie it can land an ulp off the midpoint,
+// which rounding to odd then turns into a rounding away from the even code.
+__device__ __forceinline__ uint2 nvfp4_encode16_exact(const float* v, double S) {
   float q[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    double a = fabs((double)v[i]) * R;
+    double a = S > 0.0 ? fabs((double)v[i]) / S : 0.0;
     q[i] = copysignf(round_to_odd_f32(a), v[i]);
   }
   return e2m1_encode16(q, 1.0f);

@@ -97,8 +97,7 @@ k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
       const float S32 = e4m3_value(sb[b]) * s_t;
       ok = checked_divisor(S32) && nvfp4_encode16_checked(v + 16 * b, recip_fast(S32), w[b]);
       if (!ok) {
-        const double S = (double)e4m3_value(sb[b]) * (double)s_t;     // exact
-        w[b] = nvfp4_encode16_exact(v + 16 * b, S > 0.0 ? 1.0 / S : 0.0);
+        w[b] = nvfp4_encode16_exact(v + 16 * b, (double)e4m3_value(sb[b]) * (double)s_t);   // S exact
       }
     } else {
       sb[b] = nvfp4_block_scale_fast(absmax<16>(v + 16 * b), inv6s);

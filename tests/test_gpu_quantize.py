@@ -295,3 +295,45 @@ def test_nvfp4_dynamic_scale_large_tensor(h):
     else:
         zmax = np.float32(np.max(np.abs(_np(dbg))))
         assert gst == zmax / np.float32(2688.0)
+
+
+def _near_boundary_tensor(st):
+    """Blocks whose maximum puts amax / (6 s_t) a few ulps either side of an E4M3 midpoint,
+    and whose other elements put x / (s_b s_t) a few ulps either side of an E2M1 midpoint
+    (s_b the E4M3 scale the oracle picks for the block)."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    e4m3_mids = np.array([1.0625, 1.1875, 2.125, 3.75, 17.0, 104.0, 416.0])   # between E4M3 neighbours
+    rng = np.random.default_rng(17)
+    blocks = []
+    for bm in e4m3_mids:
+        for k in (-3, -1, 0, 1, 3):
+            amax = np.float32(6.0 * float(st) * bm * (1.0 + k * 2.0 ** -23))
+            sb = F.e4m3_decode(F.e4m3_rne(np.array([float(amax) / (6.0 * float(st))])))[0]
+            blk = np.zeros(16, dtype=np.float32)
+            blk[0] = amax
+            for j in range(1, 16):
+                q = mids[(j - 1) % 7] * (1.0 + int(rng.integers(-4, 5)) * 2.0 ** -23)
+                blk[j] = np.float32(q * sb * float(st)) * rng.choice([-1.0, 1.0])
+            blocks.append(blk)
+    blocks.append(np.zeros(16, dtype=np.float32))                  # 36 blocks: 9 rows of 64
+    return np.concatenate(blocks).reshape(-1, 64)
+
+
+@pytest.mark.parametrize("s_t", [2.0 ** -10, 0.0123])
+def test_nvfp4_near_boundary_quotients_exact(s_t):
+    """fp32 values whose quotients x / (s_b s_t) sit a few ulps either side of every E2M1
+    midpoint, and block maxima whose amax / (6 s_t) sit a few ulps either side of E4M3
+    midpoints.  These are the decisions a binary32 shortcut can get wrong; every code and
+    scale must still equal the oracle's exact one."""
+    _log(f"nvfp4 near-boundary quotients s_t={s_t}")
+    st = np.float32(s_t)
+    x = _near_boundary_tensor(st)
+    ts = torch.tensor([st], dtype=torch.float32, device=DEV)
+    codes, scales, _ = fp4.fp4_quantize(torch.from_numpy(x).to(DEV), "nvfp4", 0, tensor_scale=ts, mode="given")
+    ref = nvfp4.quantize(x.astype(np.float64), tensor_scale_value=st)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rel = np.min(np.abs(np.abs(ref["elem_arg"])[..., None] - mids) / mids, axis=-1)
+    assert np.count_nonzero(rel < 2.0 ** -19) >= 300              # inside the shortcut's fallback band
+    assert np.count_nonzero((rel > 0) & (rel < 2.0 ** -20)) >= 100   # near-ties, not only ties
+    assert np.array_equal(_np(scales), ref["scales"])
+    assert np.array_equal(_np(codes), ref["packed"])
