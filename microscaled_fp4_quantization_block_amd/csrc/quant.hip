@@ -4,8 +4,8 @@
 // chunk never straddles rows and its codes are one 16-byte store).  A chunk holds whole
 // Hadamard blocks (16 or 32), one MXFP4 block or two NVFP4 blocks, so rotation, block
 // maxima, scale choice and encoding all stay in the lane's registers; the only
-// cross-lane step is the per-tensor maximum of NVFP4 (a wave reduction and one atomic
-// per wave, in a separate pass before the quantization launch).
+// cross-lane step is the per-tensor maximum of NVFP4 (a grid-stride pass before the
+// quantization launch, reduced over each workgroup before its one atomic).
 //
 // Sources: MR-GPTQ abstract (hyper.ai, Résumé) for block Hadamard before MXFP4 / NVFP4
 // quantization and online activation rotation; ARCQuant summary (gist.science, Énoncé du
