@@ -63,6 +63,9 @@ typedef enum { FP4_SCALE_COMPUTE = 0, FP4_SCALE_GIVEN = 1 } fp4_scale_mode;
  *   dbg_rotated  optional [M][K] fp32 output of the rotated values (NULL = not written)
  * Shapes: M >= 0, K >= 0, K % 32 == 0.  M*K == 0 is a no-op (NVFP4 COMPUTE writes 0).
  * Unrotated codes and scales are the exact round-to-nearest-even decisions of x/scale.
+ * Rotated input is quantized from its binary32 rotated values with binary32 scale and
+ * element arithmetic: a decision can differ from the exact one only where the real
+ * quotient lies within a few binary32 ulps of a rounding boundary.
  */
 fp4_status fp4_quantize(const void* x, fp4_dtype xt, int64_t M, int64_t K, fp4_format fmt,
                         int hadamard, uint8_t* codes, uint8_t* scales, float* tensor_scale,
