@@ -337,3 +337,29 @@ def test_nvfp4_near_boundary_quotients_exact(s_t):
     assert np.count_nonzero((rel > 0) & (rel < 2.0 ** -20)) >= 100   # near-ties, not only ties
     assert np.array_equal(_np(scales), ref["scales"])
     assert np.array_equal(_np(codes), ref["packed"])
+
+
+def test_tensor_beyond_2_31_elements():
+    """A bf16 tensor of 262,208 x 8192 = 2.15e9 elements (4.3 GB): every chunk, code and
+    element index past 2^31 must be 64-bit.  Exact MXFP4 and NVFP4 (given scale) quantize
+    and MXFP4 dequantize, checked bit for bit on sampled rows including the last."""
+    M, K = 262208, 8192
+    _log(f"large tensor {M}x{K} bf16")
+    g = torch.Generator(device=DEV).manual_seed(231)
+    x = torch.randn((M, K), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    rows = np.array([0, 1, 131071, 262143, 262144, M - 2, M - 1])
+    xs = _vals(x[torch.from_numpy(rows).to(DEV)])
+    codes, scales, _ = fp4.fp4_quantize(x, "mxfp4", 0)
+    ref = mxfp4.quantize(xs)
+    assert np.array_equal(_np(codes[torch.from_numpy(rows).to(DEV)]), ref["packed"])
+    assert np.array_equal(_np(scales[torch.from_numpy(rows).to(DEV)]), ref["scales"])
+    y = fp4.fp4_dequantize(codes, scales, None, "mxfp4", 0, torch.bfloat16)
+    want = mxfp4.dequantize(ref["packed"], ref["scales"])
+    bits = _np(y[torch.from_numpy(rows).to(DEV)].view(torch.int16)).view(np.uint16)
+    assert np.array_equal(bits, F.f32_to_bf16_bits(want.astype(np.float32)))
+    del codes, scales, y
+    ts = torch.tensor([0.0017], dtype=torch.float32, device=DEV)
+    codes, scales, _ = fp4.fp4_quantize(x, "nvfp4", 0, tensor_scale=ts, mode="given")
+    ref = nvfp4.quantize(xs, tensor_scale_value=np.float32(0.0017))
+    assert np.array_equal(_np(codes[torch.from_numpy(rows).to(DEV)]), ref["packed"])
+    assert np.array_equal(_np(scales[torch.from_numpy(rows).to(DEV)]), ref["scales"])
