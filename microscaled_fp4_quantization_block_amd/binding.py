@@ -82,6 +82,24 @@ def _dev(t, name):
     return t
 
 
+def _arg(t, name, device, shape=None, dtype=None, numel=None):
+    """Check a tensor argument the kernels will read or write through a raw pointer:
+    contiguous, on `device`, and of the given shape / dtype / minimum element count.  The
+    C ABI cannot see sizes, so a short buffer must be refused here."""
+    if t is None:
+        return None
+    _dev(t, name)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
+    return t
+
+
 def _dtype_code(dt):
     if dt == torch.float32:
         return FP4_F32
@@ -105,12 +123,18 @@ def fp4_quantize(x, fmt="mxfp4", hadamard=0, codes=None, scales=None, tensor_sca
     M, K = x.shape
     f = _fmt_code(fmt)
     block = 16 if f == FP4_NVFP4 else 32
+    dev = x.device
     if codes is None:
-        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((M, K // block), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // block), dtype=torch.uint8, device=dev)
     if f == FP4_NVFP4 and tensor_scale is None:
-        tensor_scale = torch.zeros(1, dtype=torch.float32, device=x.device)
+        tensor_scale = torch.zeros(1, dtype=torch.float32, device=dev)
+    _arg(codes, "codes", dev, (M, K // 2), torch.uint8)
+    _arg(scales, "scales", dev, (M, K // block), torch.uint8)
+    if f == FP4_NVFP4:
+        _arg(tensor_scale, "tensor_scale", dev, dtype=torch.float32, numel=1)
+    _arg(dbg_rotated, "dbg_rotated", dev, (M, K), torch.float32)
     m = FP4_SCALE_COMPUTE if mode == "compute" else FP4_SCALE_GIVEN
     _check(lib().fp4_quantize(_ptr(x), _dtype_code(x.dtype), M, K, f, int(hadamard), _ptr(codes),
                               _ptr(scales), _ptr(tensor_scale) if f == FP4_NVFP4 else None, m,
@@ -123,11 +147,31 @@ def fp4_dequantize(codes, scales, tensor_scale=None, fmt="mxfp4", inverse_hadama
     """Values [M, K] of packed codes [M, K/2] and scales, optional inverse rotation."""
     _dev(codes, "codes")
     M, K = codes.shape[0], codes.shape[1] * 2
+    dev = codes.device
+    f = _fmt_code(fmt)
+    _arg(codes, "codes", dev, dtype=torch.uint8)
+    _arg(scales, "scales", dev, (M, K // (16 if f == FP4_NVFP4 else 32)), torch.uint8)
+    if f == FP4_NVFP4:
+        if tensor_scale is None:
+            raise ValueError("NVFP4 dequantization needs tensor_scale")
+        _arg(tensor_scale, "tensor_scale", dev, dtype=torch.float32, numel=1)
     if y is None:
-        y = torch.empty((M, K), dtype=out_dtype, device=codes.device)
+        y = torch.empty((M, K), dtype=out_dtype, device=dev)
+    _arg(y, "y", dev, (M, K))
     _check(lib().fp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), M, K, _fmt_code(fmt),
                                 int(inverse_hadamard), _ptr(y), _dtype_code(y.dtype), _stream(stream)))
     return y
+
+
+def _residual_args(x, perm, gamma, dbg_normed, codes, scales, S, block):
+    M, K = x.shape
+    dev = x.device
+    _arg(x, "x", dev, dtype=torch.bfloat16)
+    _arg(perm, "perm", dev, (K,), torch.int32)
+    _arg(gamma, "gamma", dev, (K,), torch.float32)
+    _arg(dbg_normed, "dbg_normed", dev, (M, K), torch.float32)
+    _arg(codes, "codes", dev, (M, (K + S) // 2), torch.uint8)
+    _arg(scales, "scales", dev, (M, (K + S) // block), torch.uint8)
 
 
 def fp4_residual_quantize(x, perm, S, gamma=None, eps=1e-6, codes=None, scales=None,
@@ -137,14 +181,15 @@ def fp4_residual_quantize(x, perm, S, gamma=None, eps=1e-6, codes=None, scales=N
     Returns (codes [M, (K+S)/2], scales [M, (K+S)/16], tensor_scale [1])."""
     _dev(x, "x")
     M, K = x.shape
+    dev = x.device
     if codes is None:
-        codes = torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((M, (K + S) // 16), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, (K + S) // 16), dtype=torch.uint8, device=dev)
     if tensor_scale is None:
-        tensor_scale = torch.zeros(1, dtype=torch.float32, device=x.device)
-    if perm.dtype != torch.int32:
-        raise ValueError("perm must be int32")
+        tensor_scale = torch.zeros(1, dtype=torch.float32, device=dev)
+    _residual_args(x, perm, gamma, dbg_normed, codes, scales, S, 16)
+    _arg(tensor_scale, "tensor_scale", dev, dtype=torch.float32, numel=1)
     m = FP4_SCALE_COMPUTE if mode == "compute" else FP4_SCALE_GIVEN
     _check(lib().fp4_residual_quantize(_ptr(x), M, K, _ptr(gamma), float(eps), _ptr(perm), int(S),
                                        _ptr(codes), _ptr(scales), _ptr(tensor_scale), m,
@@ -163,8 +208,7 @@ def fp4_residual_quantize_mx(x, perm, S, gamma=None, eps=1e-6, codes=None, scale
         codes = torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((M, (K + S) // 32), dtype=torch.uint8, device=x.device)
-    if perm.dtype != torch.int32:
-        raise ValueError("perm must be int32")
+    _residual_args(x, perm, gamma, dbg_normed, codes, scales, S, 32)
     _check(lib().fp4_residual_quantize_mx(_ptr(x), M, K, _ptr(gamma), float(eps), _ptr(perm), int(S),
                                           _ptr(codes), _ptr(scales), _ptr(dbg_normed), _stream(stream)))
     return codes, scales
@@ -178,9 +222,11 @@ def fp4_pack(x, packed=None, dbg_rotated=None, stream=None):
     """Dual-scale FP4 message (uint8 [fp4_pack_bytes(M, K)]) of bf16 x [M, K]."""
     _dev(x, "x")
     M, K = x.shape
+    n = fp4_pack_bytes(M, K)
     if packed is None:
-        n = fp4_pack_bytes(M, K)
         packed = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    _arg(packed, "packed", x.device, dtype=torch.uint8, numel=n)
+    _arg(dbg_rotated, "dbg_rotated", x.device, (M, K), torch.float32)
     _check(lib().fp4_pack(_ptr(x), M, K, _ptr(packed), _ptr(dbg_rotated), _stream(stream)))
     return packed
 
@@ -188,8 +234,10 @@ def fp4_pack(x, packed=None, dbg_rotated=None, stream=None):
 def fp4_unpack(packed, M, K, y=None, stream=None):
     """bf16 [M, K] reconstruction of a dual-scale FP4 message."""
     _dev(packed, "packed")
+    _arg(packed, "packed", packed.device, dtype=torch.uint8, numel=fp4_pack_bytes(M, K))
     if y is None:
         y = torch.empty((M, K), dtype=torch.bfloat16, device=packed.device)
+    _arg(y, "y", packed.device, (M, K), torch.bfloat16)
     _check(lib().fp4_unpack(_ptr(packed), M, K, _ptr(y), _stream(stream)))
     return y
 
@@ -202,8 +250,14 @@ def fp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16, c=N
     N = b_codes.shape[0]
     if b_codes.shape[1] * 2 != K:
         raise ValueError("A and B disagree on K")
+    dev = a_codes.device
+    _arg(a_codes, "a_codes", dev, dtype=torch.uint8)
+    _arg(b_codes, "b_codes", dev, dtype=torch.uint8)
+    _arg(a_scales, "a_scales", dev, (M, K // 32), torch.uint8)
+    _arg(b_scales, "b_scales", dev, (N, K // 32), torch.uint8)
     if c is None:
-        c = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+        c = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _arg(c, "c", dev, (M, N))
     _check(lib().fp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
                           _ptr(c), _dtype_code(c.dtype), _stream(stream)))
     return c
