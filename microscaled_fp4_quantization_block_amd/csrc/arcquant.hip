@@ -40,6 +40,12 @@ constexpr int kStage = 8;           // permutation entries per thread staged in 
 // rows with the next row's loads in flight.
 constexpr int kPipeWaves = 8;
 constexpr int kPipeTotal = 4096;
+// With a gain vector the pipelined kernel also keeps gamma (K floats) in LDS, once per
+// workgroup: 7 waves per workgroup keep two workgroups per CU within the LDS, and the
+// staging batch grows to cover K = 4096 with 448 threads.
+constexpr int kGammaWaves = 7;
+constexpr int kGammaStage = 10;
+constexpr int kGammaTotal = 3584;                      // 512 workgroups of 7 waves
 // Statistics passes end in one atomic maximum per workgroup; atomics on one address
 // serialise, so their grids are capped at kStatsGroups workgroups.
 constexpr int kStatsGroups = 256;
@@ -284,11 +290,18 @@ __device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], floa
 // kBlocks blocks per lane are gathered together (all their LDS reads in flight at once)
 // before any of them is encoded.
 constexpr int kBlocks = 1;
+// gl: gamma in channel order in LDS (byte offset of channel c = 2 x its offset in the
+// bf16 row), or null to read gamma from global memory.
+template <bool kGamma>
+__device__ __forceinline__ float gain_at(const float* gl, const float* __restrict__ gamma, uint32_t off) {
+  return gl ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gl) + 2 * off) : gamma[off >> 1];
+}
+
 template <bool kGamma>
 __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
-                                           int lane, float inv_rms, const float* __restrict__ gamma, float s_t,
-                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                           float* __restrict__ dbg) {
+                                           int lane, float inv_rms, const float* __restrict__ gamma,
+                                           const float* gl, float s_t, uint8_t* __restrict__ codes,
+                                           uint8_t* __restrict__ scales, float* __restrict__ dbg) {
   const int nblk = K / 16, sblk = S / 16;
   const int64_t row_codes = (K + S) / 2, row_scales = (K + S) / 16;
   uint8_t* crow = codes + r * row_codes;
@@ -322,8 +335,8 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
         float g[16];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          g[2 * k] = gamma[(w[k] & 0xFFFFu) >> 1];
-          g[2 * k + 1] = gamma[w[k] >> 17];
+          g[2 * k] = gain_at<true>(gl, gamma, w[k] & 0xFFFFu);
+          g[2 * k + 1] = gain_at<true>(gl, gamma, w[k] >> 16);
         }
         float z[16];
 #pragma unroll
@@ -353,6 +366,7 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
 template <bool kGamma>
 __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
                                               int lane, float inv_rms, const float* __restrict__ gamma,
+                                              const float* gl,
                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                               float* __restrict__ dbg) {
   const int nblk = K / 32, sblk = S / 32;
@@ -375,7 +389,7 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
     }
     float g[32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gamma[c[k] >> 1] : 1.0f;
+    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gain_at<true>(gl, gamma, (uint32_t)c[k]) : 1.0f;
     float z[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k)
@@ -408,44 +422,60 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  uint16_t* ps = smem;                                   // [K] permutation, as byte offsets 2 perm[c]
-  uint16_t* xs = smem + (size_t)(1 + wave) * K;          // [K] this wave's row
-
   const int units = K / 8;
+  const bool pipelined = units <= 64 * kUnroll;
+  // LDS: [K] permutation as byte offsets 2 perm[c]; with a gain vector and short rows,
+  // [K] fp32 gamma in channel order; then one [K] bf16 row per wave.
+  const bool lds_gamma = kGamma && pipelined;
+  uint16_t* ps = smem;
+  float* gl = lds_gamma ? reinterpret_cast<float*>(smem + K) : nullptr;
+  uint16_t* xs = smem + (size_t)(lds_gamma ? 3 : 1) * K + (size_t)wave * K;
+
   const int64_t stride = (int64_t)gridDim.x * W;
   int64_t r = (int64_t)blockIdx.x * W + wave;
-  const bool pipelined = units <= 64 * kUnroll;
   // An index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced.
+  constexpr int kSt = kGamma ? kGammaStage : kStage;
   uint4 raw[kUnroll];
-  if (pipelined && K <= kStage * (int)blockDim.x) {
+  if (pipelined && K <= kSt * (int)blockDim.x) {
     // The permutation's loads (L2-resident after the first workgroups) go out first, then
     // the first row's.  The permutation is written to LDS as soon as its own loads land and
     // the barrier waits for those LDS writes only, so the row stays in flight meanwhile.
     // Indices are clamped so that every load is issued (a row past M reloads row M - 1,
     // which is then never used).
-    uint32_t pv[kStage];
+    uint32_t pv[kSt];
+    float gv[kGamma ? kSt : 1];
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) pv[i] = (uint32_t)perm[min((int)threadIdx.x + i * (int)blockDim.x, K - 1)];
+    for (int i = 0; i < kSt; ++i) {
+      const int c = min((int)threadIdx.x + i * (int)blockDim.x, K - 1);
+      pv[i] = (uint32_t)perm[c];
+      if constexpr (kGamma) gv[i] = gamma[c];                // coalesced, channel order
+    }
     load_units_rsrc(x + (r < M ? r : M - 1) * K, units, lane, raw);   // pipelined: one chunk
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
+    for (int i = 0; i < kSt; ++i) {
       const int c = threadIdx.x + i * blockDim.x;
-      if (c < K) ps[c] = (uint16_t)(2 * min(pv[i], (uint32_t)(K - 1)));
+      if (c < K) {
+        ps[c] = (uint16_t)(2 * min(pv[i], (uint32_t)(K - 1)));
+        if constexpr (kGamma) gl[c] = gv[i];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt left open
     __builtin_amdgcn_s_barrier();
   } else {
     if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
-    for (int c = threadIdx.x; c < K; c += blockDim.x) ps[c] = (uint16_t)(2 * min((uint32_t)perm[c], (uint32_t)(K - 1)));
+    for (int c = threadIdx.x; c < K; c += blockDim.x) {
+      ps[c] = (uint16_t)(2 * min((uint32_t)perm[c], (uint32_t)(K - 1)));
+      if (lds_gamma) gl[c] = gamma[c];
+    }
     __syncthreads();
   }
 
   const float s_t = FMT == fp4impl::FMT_NV ? *tensor_scale : 0.0f;
   auto encode = [&](int64_t row, float inv_rms) {
     if constexpr (FMT == fp4impl::FMT_NV)
-      encode_row<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, s_t, codes, scales, dbg);
+      encode_row<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, s_t, codes, scales, dbg);
     else
-      encode_row_mx<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, codes, scales, dbg);
+      encode_row_mx<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, codes, scales, dbg);
   };
   if (pipelined) {
     // whole row in one chunk: the next row's loads are in flight while this row is encoded
@@ -483,17 +513,19 @@ struct ArcLaunch {
   size_t lds_stats, lds_quant;
 };
 
-ArcLaunch arc_launch(int64_t M, int64_t K) {
+ArcLaunch arc_launch(int64_t M, int64_t K, bool gamma) {
   ArcLaunch a;
   a.W = waves_for(K);
   const int64_t rows_per_grid = 1024 * (int64_t)a.W;     // at most 1024 workgroups, persistent beyond
   a.grid = (unsigned)(M <= 0 ? 1 : (M < rows_per_grid ? (M + a.W - 1) / a.W : 1024));
   const bool pipelined = K / 8 <= 64 * kUnroll;
-  a.Wq = pipelined ? kPipeWaves : a.W;
-  const int64_t wq_total = pipelined ? (M < kPipeTotal ? M : kPipeTotal) : (M < rows_per_grid ? M : rows_per_grid);
+  const bool lds_gamma = gamma && pipelined;
+  a.Wq = pipelined ? (lds_gamma ? kGammaWaves : kPipeWaves) : a.W;
+  const int64_t total = lds_gamma ? kGammaTotal : kPipeTotal;
+  const int64_t wq_total = pipelined ? (M < total ? M : total) : (M < rows_per_grid ? M : rows_per_grid);
   a.grid_q = (unsigned)(wq_total <= 0 ? 1 : (wq_total + a.Wq - 1) / a.Wq);
   a.lds_stats = (size_t)2 * K * a.W;
-  a.lds_quant = (size_t)2 * K * (a.Wq + 1);
+  a.lds_quant = (size_t)2 * K * (a.Wq + 1) + (lds_gamma ? (size_t)4 * K : 0);
   return a;
 }
 
@@ -503,7 +535,7 @@ template <int FMT, bool kGamma>
 hipError_t launch_arc(const uint16_t* x, int64_t M, int64_t K, const float* gamma, float eps, const int32_t* perm,
                       int64_t S, uint8_t* codes, uint8_t* scales, float* ts, bool compute, float* dbg,
                       hipStream_t st) {
-  const ArcLaunch a = arc_launch(M, K);
+  const ArcLaunch a = arc_launch(M, K, kGamma);
   hipError_t e = allow_lds(reinterpret_cast<const void*>(k_arcquant<FMT, kGamma>), a.lds_quant);
   if (e == hipSuccess && compute && K / 8 > 64 * kUnroll)
     e = allow_lds(reinterpret_cast<const void*>(k_arc_stats<kGamma>), a.lds_stats);

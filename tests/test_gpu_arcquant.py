@@ -86,7 +86,8 @@ def test_arcquant_config_full_size():
     print(f"  boundary-tolerated code differences: {n}", flush=True)
 
 
-@pytest.mark.parametrize("M,K,S,gam", [(9000, 256, 64, False), (40, 8192, 512, False), (37, 12288, 256, True)])
+@pytest.mark.parametrize("M,K,S,gam", [(9000, 256, 64, False), (40, 8192, 512, False), (37, 12288, 256, True),
+                                       (5000, 1024, 128, True)])
 def test_arcquant_multi_row_and_long_rows(M, K, S, gam):
     """More rows than resident waves (each wave walks several rows, prefetching the next)
     and rows longer than one 4096-channel chunk (the row streams in several chunks)."""
