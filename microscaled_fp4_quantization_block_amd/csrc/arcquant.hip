@@ -34,18 +34,14 @@ namespace {
 constexpr int kMaxWaves = 8;
 constexpr int kLdsLimit = 144 * 1024;       // dynamic LDS per workgroup used here
 constexpr int kUnroll = 8;          // 16-byte loads in flight per lane
-constexpr int kStage = 8;           // permutation entries per thread staged in one batch
-// Rows of at most 64 kUnroll 16-byte units are software-pipelined: kPipeWaves waves per
-// workgroup and at most kPipeTotal waves in all (16 per CU), each walking several
-// rows with the next row's loads in flight.
-constexpr int kPipeWaves = 8;
+// Rows of at most 64 kUnroll 16-byte units (K <= kPipeK) are software-pipelined: at most
+// kPipeTotal waves in all (16 per CU), each walking several rows with the next row's
+// loads in flight.  Without a gain vector, 8 waves per workgroup (two workgroups per
+// CU); with one, 16 (one per CU), so that gamma (K floats) sits in LDS once per CU.
+constexpr int kPipeK = 8 * 64 * kUnroll;
 constexpr int kPipeTotal = 4096;
-// With a gain vector the pipelined kernel also keeps gamma (K floats) in LDS, once per
-// workgroup: 7 waves per workgroup keep two workgroups per CU within the LDS, and the
-// staging batch grows to cover K = 4096 with 448 threads.
-constexpr int kGammaWaves = 7;
-constexpr int kGammaStage = 10;
-constexpr int kGammaTotal = 3584;                      // 512 workgroups of 7 waves
+template <bool kGamma>
+constexpr int pipe_waves() { return kGamma ? 16 : 8; }
 // Statistics passes end in one atomic maximum per workgroup; atomics on one address
 // serialise, so their grids are capped at kStatsGroups workgroups.
 constexpr int kStatsGroups = 256;
@@ -275,11 +271,15 @@ __device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], floa
   *reinterpret_cast<uint2*>(crow + 8 * b) = w;
   srow[b] = (uint8_t)sb;
   if (b < sblk) {
+    // z = fl(x inv_rms) is formed here, not shared with the debug copy: shared, the
+    // compiler hoists its 16 products above both branches into every block.
+    float ir = inv_rms;
+    asm volatile("" : "+v"(ir));
     float q[16];
     e2m1_decode8(w.x, 1.0f, q);
     e2m1_decode8(w.y, 1.0f, q + 8);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, x[i] * inv_rms);   // z - V s_b s_t
+    for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, x[i] * ir);   // z - V s_b s_t
     const uint32_t sr = nvfp4_block_scale_fast(absmax<16>(q), inv6s);
     *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t));
     srow[nblk + b] = (uint8_t)sr;
@@ -415,7 +415,7 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
 }
 
 template <int FMT, bool kGamma>
-__global__ void __launch_bounds__(64 * kMaxWaves)
+__global__ void __launch_bounds__(64 * pipe_waves<kGamma>())
 k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ gamma, float eps,
            const int32_t* __restrict__ perm, int S, uint8_t* __restrict__ codes,
            uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, float* __restrict__ dbg) {
@@ -434,14 +434,16 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   const int64_t stride = (int64_t)gridDim.x * W;
   int64_t r = (int64_t)blockIdx.x * W + wave;
   // An index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced.
-  constexpr int kSt = kGamma ? kGammaStage : kStage;
+  constexpr int kSt = kPipeK / (64 * pipe_waves<kGamma>());   // staging batch per thread
   uint4 raw[kUnroll];
   if (pipelined && K <= kSt * (int)blockDim.x) {
-    // The permutation's loads (L2-resident after the first workgroups) go out first, then
-    // the first row's.  The permutation is written to LDS as soon as its own loads land and
-    // the barrier waits for those LDS writes only, so the row stays in flight meanwhile.
-    // Indices are clamped so that every load is issued (a row past M reloads row M - 1,
-    // which is then never used).
+    // The permutation's loads (L2-resident after the first workgroups) go out first.  The
+    // first half of the waves then issue their rows' loads at once; the second half issue
+    // theirs only after the barrier, which the first half pass once their rows have
+    // landed.  Rows then land in two waves of traffic, and the first half is encoded
+    // while the second half is still arriving: with every row requested at once, all of
+    // them would land together at the end and the encode would start only then.  A row
+    // past M reloads row M - 1, which is then never used, so every wave takes part.
     uint32_t pv[kSt];
     float gv[kGamma ? kSt : 1];
 #pragma unroll
@@ -450,7 +452,9 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
       pv[i] = (uint32_t)perm[c];
       if constexpr (kGamma) gv[i] = gamma[c];                // coalesced, channel order
     }
-    load_units_rsrc(x + (r < M ? r : M - 1) * K, units, lane, raw);   // pipelined: one chunk
+    const int64_t r0 = r < M ? r : M - 1;
+    const bool early = wave < (W >> 1);
+    if (early) load_units_rsrc(x + r0 * K, units, lane, raw);   // pipelined: one chunk
 #pragma unroll
     for (int i = 0; i < kSt; ++i) {
       const int c = threadIdx.x + i * blockDim.x;
@@ -459,8 +463,9 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
         if constexpr (kGamma) gl[c] = gv[i];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt left open
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): own row landed, LDS written
     __builtin_amdgcn_s_barrier();
+    if (!early) load_units_rsrc(x + r0 * K, units, lane, raw);
   } else {
     if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
     for (int c = threadIdx.x; c < K; c += blockDim.x) {
@@ -520,9 +525,8 @@ ArcLaunch arc_launch(int64_t M, int64_t K, bool gamma) {
   a.grid = (unsigned)(M <= 0 ? 1 : (M < rows_per_grid ? (M + a.W - 1) / a.W : 1024));
   const bool pipelined = K / 8 <= 64 * kUnroll;
   const bool lds_gamma = gamma && pipelined;
-  a.Wq = pipelined ? (lds_gamma ? kGammaWaves : kPipeWaves) : a.W;
-  const int64_t total = lds_gamma ? kGammaTotal : kPipeTotal;
-  const int64_t wq_total = pipelined ? (M < total ? M : total) : (M < rows_per_grid ? M : rows_per_grid);
+  a.Wq = pipelined ? (gamma ? pipe_waves<true>() : pipe_waves<false>()) : a.W;
+  const int64_t wq_total = pipelined ? (M < kPipeTotal ? M : kPipeTotal) : (M < rows_per_grid ? M : rows_per_grid);
   a.grid_q = (unsigned)(wq_total <= 0 ? 1 : (wq_total + a.Wq - 1) / a.Wq);
   a.lds_stats = (size_t)2 * K * a.W;
   a.lds_quant = (size_t)2 * K * (a.Wq + 1) + (lds_gamma ? (size_t)4 * K : 0);
