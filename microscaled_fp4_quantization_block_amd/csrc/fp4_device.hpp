@@ -233,9 +233,12 @@ __device__ __forceinline__ uint32_t e4m3_rne(double r) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// Value of an E4M3 code (OCP E4M3FN: 2^(e-7) (1 + m/8), subnormals m 2^-9) by the
+// hardware convert, exact for every code; the byte is the low one of `code`.  The same
+// instruction family encodes the scales (v_cvt_pk_fp8_f32), so both ends use the same
+// format on gfx950.
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
-  uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  return e == 0 ? (float)m * 0x1p-9f : ldexpf((float)(8u + m), (int)e - 10);
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
 // NVFP4 block scale decision for block maximum amax under tensor scale s_t:
@@ -315,9 +318,11 @@ __device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
   return (uint32_t)(e + 127);
 }
 
-// 2^(code - 127) as a binary32 (code 0 is the subnormal 2^-127).
+// 2^(code - 127) as a binary32 (code 0 is the subnormal 2^-127; 0xFF is the format's NaN,
+// never produced by e8m0_from_amax).
 __device__ __forceinline__ float e8m0_value(uint32_t code) {
-  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+  const float v = code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+  return code == 0xFFu ? __uint_as_float(0x7FC00000u) : v;
 }
 
 // --------------------------------------------------------------------------- DPP quads

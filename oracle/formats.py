@@ -158,9 +158,10 @@ E2M1_EMAX = 2
 
 
 def e8m0_decode(code):
-    """2^(code - 127) as fp64 (0xFF, NaN in the format, is never produced here)."""
+    """2^(code - 127) as fp64; 0xFF is the format's NaN (OCP MX v1.0), never produced by
+    e8m0_from_amax, only met when decoding foreign scale bytes."""
     code = np.asarray(code, dtype=np.int64)
-    return np.ldexp(1.0, code - E8M0_BIAS)
+    return np.where(code == 255, np.nan, np.ldexp(1.0, code - E8M0_BIAS))
 
 
 def e8m0_from_amax(amax):

@@ -217,6 +217,32 @@ def test_dequantize_every_variant(fmt, h, out):
         P.assert_bf16_close(got, want, h, what="dequantized + inverse H, bf16")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_dequantize_every_scale_byte(fmt):
+    """Dequantization decodes every scale byte as the format defines it, including the ones
+    quantization never writes: E4M3 bytes with the sign bit (negative scales) and its two
+    NaN encodings 0x7F / 0xFF, and E8M0's NaN 0xFF.  Row r carries scale bytes r and 255 - r
+    over blocks holding every E2M1 code; bit-exact against the oracle, NaN where it has NaN."""
+    blk = 16 if fmt == "nvfp4" else 32
+    _log(f"every scale byte {fmt}")
+    M, K = 256, 2 * blk if blk == 32 else 32
+    r = np.arange(M, dtype=np.uint8)
+    scales = np.stack([r, 255 - r], axis=1).astype(np.uint8)
+    nib = (np.arange(K) % 16).astype(np.uint8)
+    packed = F.pack_nibbles(np.tile(nib, (M, 1)))
+    ts = np.float32(0.37)
+    y = fp4.fp4_dequantize(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV),
+                           torch.tensor([ts], device=DEV) if fmt == "nvfp4" else None, fmt, 0, torch.float32)
+    want = (nvfp4.dequantize(packed, scales, ts) if fmt == "nvfp4" else mxfp4.dequantize(packed, scales))
+    got = _np(y)
+    with np.errstate(over="ignore"):                       # 6 x 2^127 overflows, on both sides
+        want32 = want.astype(np.float32)
+    nan = np.isnan(want32)
+    assert nan.any()
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want32[~nan].view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt,h", [("mxfp4", 32), ("mxfp4", 16), ("nvfp4", 16), ("nvfp4", 32)])
 def test_rotated_fp32_input(fmt, h):
     """fp32 input (not only bf16) through the rotated quantizers: rotated values, scales

@@ -139,9 +139,13 @@ def test_e4m3_against_exact_bruteforce():
 # ----------------------------------------------------------------------------- E8M0
 
 def test_e8m0_decode_matches_torch():
-    codes = np.arange(255, dtype=np.uint8)               # 0xFF is NaN
+    codes = np.arange(256, dtype=np.uint8)
     ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
-    assert np.array_equal(ref, F.e8m0_decode(codes))
+    got = F.e8m0_decode(codes)
+    nan = np.isnan(ref)
+    assert nan.tolist() == [False] * 255 + [True]       # 0xFF is the format's NaN
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
 
 
 def test_e8m0_from_amax_golden():
