@@ -42,6 +42,7 @@ constexpr int kPipeK = 8 * 64 * kUnroll;
 constexpr int kPipeTotal = 4096;
 template <bool kGamma>
 constexpr int pipe_waves() { return kGamma ? 16 : 8; }
+constexpr int kMaxGroups = 8;       // load groups of two waves, at most 16 waves
 // Statistics passes end in one atomic maximum per workgroup; atomics on one address
 // serialise, so their grids are capped at kStatsGroups workgroups.
 constexpr int kStatsGroups = 256;
@@ -438,12 +439,14 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   uint4 raw[kUnroll];
   if (pipelined && K <= kSt * (int)blockDim.x) {
     // The permutation's loads (L2-resident after the first workgroups) go out first.  The
-    // first half of the waves then issue their rows' loads at once; the second half issue
-    // theirs only after the barrier, which the first half pass once their rows have
-    // landed.  Rows then land in two waves of traffic, and the first half is encoded
-    // while the second half is still arriving: with every row requested at once, all of
-    // them would land together at the end and the encode would start only then.  A row
-    // past M reloads row M - 1, which is then never used, so every wave takes part.
+    // rows are then requested in groups of two waves: group 0 at once, group g once both
+    // waves of group g - 1 have the first half of their rows in (an LDS counter per
+    // group).  Rows thus land in a steady stream, and each group is encoded while the
+    // next ones arrive: with every row requested at once, all of them would land together
+    // at the end and the encode would start only then.  Group 0 waits for nothing, every
+    // wave counts itself unconditionally, and every group but possibly the last has two
+    // waves, so every wait ends.  A row past M reloads row M - 1, which is then never
+    // used, so every wave takes part.
     uint32_t pv[kSt];
     float gv[kGamma ? kSt : 1];
 #pragma unroll
@@ -452,9 +455,11 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
       pv[i] = (uint32_t)perm[c];
       if constexpr (kGamma) gv[i] = gamma[c];                // coalesced, channel order
     }
+    __shared__ uint32_t landed[kMaxGroups];
     const int64_t r0 = r < M ? r : M - 1;
-    const bool early = wave < (W >> 1);
-    if (early) load_units_rsrc(x + r0 * K, units, lane, raw);   // pipelined: one chunk
+    const int grp = wave >> 1;
+    if (threadIdx.x < kMaxGroups) landed[threadIdx.x] = 0u;
+    if (grp == 0) load_units_rsrc(x + r0 * K, units, lane, raw);   // pipelined: one chunk
 #pragma unroll
     for (int i = 0; i < kSt; ++i) {
       const int c = threadIdx.x + i * blockDim.x;
@@ -463,9 +468,15 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
         if constexpr (kGamma) gl[c] = gv[i];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): own row landed, LDS written
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): table and counters written
     __builtin_amdgcn_s_barrier();
-    if (!early) load_units_rsrc(x + r0 * K, units, lane, raw);
+    if (grp > 0) {
+      while (__hip_atomic_load(&landed[grp - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 2u)
+        __builtin_amdgcn_s_sleep(1);
+      load_units_rsrc(x + r0 * K, units, lane, raw);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): the first 4 of the row's 8 loads are in
+    if (lane == 0) atomicAdd(&landed[grp], 1u);
   } else {
     if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
     for (int c = threadIdx.x; c < K; c += blockDim.x) {
