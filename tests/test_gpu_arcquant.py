@@ -126,3 +126,37 @@ def test_dynamic_scale_matches_quantizing_pass(M, K, gam):
     assert _np(ts)[0] == zmax / np.float32(2688.0)
     rows = np.unique(np.concatenate([W.seeded_rows(M, min(M, 24), 3), [0, M - 1]]))
     _check_arc(xt, perm, 16, gamma=gamma, rows=rows)
+
+
+def _degenerate(K, seed):
+    """Rows with nothing to normalise against: all zero, one spike, constant, alternating
+    signs, Gaussian, tiny (10^-30, far below the tensor's grid), and one with 2^-120
+    elements next to a spike of 300.  The gain has zeros (signed zeros reach the codes) and
+    negative entries; the permutation is random."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((7, K))
+    x[1, 7] = 3.0
+    x[2, :] = 0.75
+    x[3, :] = np.where(np.arange(K) % 2, 1.5, -1.5)
+    x[4, :] = rng.standard_normal(K)
+    x[5, :] = 1e-30 * rng.standard_normal(K)
+    x[6, :] = 2.0 ** -120
+    x[6, K // 2] = 300.0
+    gamma = rng.uniform(-1.5, 1.5, K)
+    gamma[rng.choice(K, K // 8, replace=False)] = 0.0
+    return W.to_bf16(x), gamma, rng.permutation(K).astype(np.int32)
+
+
+@pytest.mark.parametrize("K,gam", [(512, False), (512, True), (8192, True)])
+def test_arcquant_degenerate_rows(K, gam):
+    print(f"arcquant degenerate rows K={K} gamma={gam}", flush=True)
+    xt, gamma, perm = _degenerate(K, K + 5)
+    _check_arc(xt, perm, 64, gamma=gamma if gam else None)
+
+
+def test_arcquant_all_zero_tensor():
+    """max|z| = 0: the computed tensor scale is exactly 0, and every code and scale is 0."""
+    xt = W.to_bf16(np.zeros((5, 256)))
+    codes, scales, ts = fp4.fp4_residual_quantize(xt.to(DEV), torch.arange(256, dtype=torch.int32, device=DEV), 32)
+    assert _np(ts)[0] == 0.0 and not np.signbit(_np(ts)[0])
+    assert not _np(codes).any() and not _np(scales).any()

@@ -105,3 +105,13 @@ def test_augmented_gemm_end_to_end():
     e_plain = np.linalg.norm(_np(cp).astype(np.float64) - exact)
     print(f"  |C - yW^T|: augmented {e_aug:.4g}, primary only {e_plain:.4g}", flush=True)
     assert e_aug < e_plain
+
+
+@pytest.mark.parametrize("K,gam", [(512, False), (512, True), (8192, True)])
+def test_arcquant_mx_degenerate_rows(K, gam):
+    """The NVFP4 test's degenerate rows (all zero, spike, constant, alternating, tiny,
+    2^-120 beside a spike) with a gain holding zeros and negative entries."""
+    from tests.test_gpu_arcquant import _degenerate
+    print(f"arcquant mx degenerate rows K={K} gamma={gam}", flush=True)
+    xt, gamma, perm = _degenerate(K, K + 9)
+    _check_arc_mx(xt, perm, 64, gamma=gamma if gam else None)
