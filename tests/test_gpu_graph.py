@@ -83,6 +83,26 @@ def test_graph_residual_quantize_dynamic_scale():
     _replays_match(run, [codes, scales, ts])
 
 
+def test_graph_residual_quantize_gamma_nvfp4_and_mxfp4():
+    """Both residual flavours with a gain vector (one 16-wave workgroup per CU, gamma in
+    LDS) and a given NVFP4 tensor scale."""
+    print("graph arcquant gamma 300x4096 S=256, nvfp4 given scale + mxfp4", flush=True)
+    rng = np.random.default_rng(6)
+    x = W.to_bf16(rng.standard_normal((300, 4096))).to(DEV)
+    perm = torch.from_numpy(rng.permutation(4096).astype(np.int32)).to(DEV)
+    gamma = torch.from_numpy(rng.uniform(0.5, 1.5, 4096).astype(np.float32)).to(DEV)
+    ts = torch.tensor([0.004], dtype=torch.float32, device=DEV)
+    c_nv = torch.empty((300, (4096 + 256) // 2), dtype=torch.uint8, device=DEV)
+    s_nv = torch.empty((300, (4096 + 256) // 16), dtype=torch.uint8, device=DEV)
+    c_mx = torch.empty((300, (4096 + 256) // 2), dtype=torch.uint8, device=DEV)
+    s_mx = torch.empty((300, (4096 + 256) // 32), dtype=torch.uint8, device=DEV)
+
+    def run():
+        fp4.fp4_residual_quantize(x, perm, 256, gamma=gamma, codes=c_nv, scales=s_nv, tensor_scale=ts, mode="given")
+        fp4.fp4_residual_quantize_mx(x, perm, 256, gamma=gamma, codes=c_mx, scales=s_mx)
+    _replays_match(run, [c_nv, s_nv, c_mx, s_mx])
+
+
 def test_graph_pack_unpack():
     print("graph pack/unpack 256x1024", flush=True)
     x = W.to_bf16(np.random.default_rng(3).standard_t(4, (256, 1024))).to(DEV)
