@@ -295,14 +295,17 @@ __device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], floa
 // kBlocks blocks per lane are gathered together (all their LDS reads in flight at once)
 // before any of them is encoded.
 constexpr int kBlocks = 1;
-// gl: gamma in channel order in LDS (byte offset of channel c = 2 x its offset in the
-// bf16 row), or null to read gamma from global memory.
-template <bool kGamma>
+// Gain of the channel at byte offset `off` of the bf16 row: from gl, gamma in channel order
+// in LDS (its byte offset is 2 off), when kLds, else from global memory.  Where gamma lives
+// is a template parameter: a run-time choice per element compiles to flat loads behind
+// address selects.
+template <bool kLds>
 __device__ __forceinline__ float gain_at(const float* gl, const float* __restrict__ gamma, uint32_t off) {
-  return gl ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gl) + 2 * off) : gamma[off >> 1];
+  if constexpr (kLds) return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gl) + 2 * off);
+  else return gamma[off >> 1];
 }
 
-template <bool kGamma>
+template <bool kGamma, bool kLdsGamma>
 __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
                                            int lane, float inv_rms, const float* __restrict__ gamma,
                                            const float* gl, float s_t, uint8_t* __restrict__ codes,
@@ -340,8 +343,8 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
         float g[16];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          g[2 * k] = gain_at<true>(gl, gamma, w[k] & 0xFFFFu);
-          g[2 * k + 1] = gain_at<true>(gl, gamma, w[k] >> 16);
+          g[2 * k] = gain_at<kLdsGamma>(gl, gamma, w[k] & 0xFFFFu);
+          g[2 * k + 1] = gain_at<kLdsGamma>(gl, gamma, w[k] >> 16);
         }
         float z[16];
 #pragma unroll
@@ -368,7 +371,7 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
 // by the hardware convert (exact: power-of-two scale).  The residual z - V 2^(e-127) is
 // exact in binary32: z lies within a factor of two of its nearest grid point, or the
 // grid point is 0.  Lane l takes blocks l, l + 64, ...
-template <bool kGamma>
+template <bool kGamma, bool kLdsGamma>
 __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t* ps, int64_t r, int K, int S,
                                               int lane, float inv_rms, const float* __restrict__ gamma,
                                               const float* gl,
@@ -394,7 +397,7 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
     }
     float g[32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gain_at<true>(gl, gamma, (uint32_t)c[k]) : 1.0f;
+    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gain_at<kLdsGamma>(gl, gamma, (uint32_t)c[k]) : 1.0f;
     float z[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k)
@@ -433,7 +436,7 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   // [K] fp32 gamma in channel order; then one [K] bf16 row per wave.
   const bool lds_gamma = kGamma && pipelined;
   uint16_t* ps = smem;
-  float* gl = lds_gamma ? reinterpret_cast<float*>(smem + K) : nullptr;
+  float* gl = reinterpret_cast<float*>(smem + K);   // used only when lds_gamma
   uint16_t* xs = smem + (size_t)(lds_gamma ? 3 : 1) * K + (size_t)wave * K;
 
   const int64_t stride = (int64_t)gridDim.x * W;
@@ -492,10 +495,17 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
 
   const float s_t = FMT == fp4impl::FMT_NV ? *tensor_scale : 0.0f;
   auto encode = [&](int64_t row, float inv_rms) {
-    if constexpr (FMT == fp4impl::FMT_NV)
-      encode_row<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, s_t, codes, scales, dbg);
-    else
-      encode_row_mx<kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, codes, scales, dbg);
+    if constexpr (FMT == fp4impl::FMT_NV) {
+      if (kGamma && lds_gamma)
+        encode_row<kGamma, kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, s_t, codes, scales, dbg);
+      else
+        encode_row<kGamma, false>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, s_t, codes, scales, dbg);
+    } else {
+      if (kGamma && lds_gamma)
+        encode_row_mx<kGamma, kGamma>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, codes, scales, dbg);
+      else
+        encode_row_mx<kGamma, false>(xs, ps, row, K, S, lane, inv_rms, gamma, gl, codes, scales, dbg);
+    }
   };
   if (pipelined) {
     // whole row in one chunk: the next row's loads are in flight while this row is encoded
