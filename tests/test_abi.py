@@ -124,3 +124,13 @@ def test_empty_shapes_are_no_ops():
     assert _status("fp4_residual_quantize_mx", None, 0, 64, None, ctypes.c_float(1e-6), FAKE, 32, None, None,
                    None, None)[0] == 0
     assert _status("fp4_gemm", None, None, None, None, 0, 5, 128, None, 1, None)[0] == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without libfp4.so the first call raises instead of computing anywhere else."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_LIB_PATH", os.path.join(ROOT, "no_such_dir", "libfp4.so"))
+    with pytest.raises(RuntimeError, match="HIP library missing"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="HIP library missing"):
+        B.fp4_pack_bytes(4, 128)
