@@ -60,13 +60,21 @@ def check_e4m3_scales(gpu, ref, ref_arg, tol=TOL, what="E4M3 scales"):
     return int(np.sum(gpu != ref))
 
 
+def e8m0_boundary_distance(amax):
+    """Relative distance |amax - 2^k| / 2^k of a block maximum to the nearest power of two:
+    the E8M0 code floor(log2 amax) - 2 changes only where amax crosses one.  With
+    amax = f 2^E (f in [0.5, 1), exact from frexp) the candidates are 2^(E-1), at 2f - 1,
+    and 2^E, at 1 - f; both differences are exact in float64.  An all-zero block
+    (amax = 0) has no neighbouring decision: inf."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, _ = np.frexp(a)
+    return np.where(a > 0, np.minimum(2.0 * f - 1.0, 1.0 - f), np.inf)
+
+
 def check_e8m0_scales(gpu, ref, ref_amax, tol=TOL, what="E8M0 scales"):
     gpu = np.asarray(gpu, dtype=np.int64)
     ref = np.asarray(ref, dtype=np.int64)
-    a = np.asarray(ref_amax, dtype=np.float64)
-    with np.errstate(divide="ignore"):
-        l2 = np.log2(np.where(a > 0, a, 1.0))
-    near = np.abs(l2 - np.round(l2)) <= tol / np.log(2)
+    near = e8m0_boundary_distance(ref_amax) <= tol
     ok = (gpu == ref) | ((np.abs(gpu - ref) == 1) & near)
     assert ok.all(), (f"{what}: {np.sum(~ok)} differ away from a power of two; first at "
                       f"{np.argwhere(~ok)[0]}: gpu={gpu[~ok][0]} ref={ref[~ok][0]}")
