@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/fp4.h"
@@ -32,6 +33,20 @@ fp4_status hip_status(hipError_t e, const char* where) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Host-side fault injection for testing the error path without a GPU: with the
+// environment variable FP4_FAULT_INJECT=launch, every entry point that passes its
+// argument validation reports a launch failure through the same status mapping as a
+// real one, and enqueues nothing.  Read on every call, so a test can switch it.
+bool launch_failure_injected() {
+  const char* v = std::getenv("FP4_FAULT_INJECT");
+  return v != nullptr && std::strcmp(v, "launch") == 0;
+}
+
+#define INJECT_POINT(where)                                                                   \
+  do {                                                                                        \
+    if (launch_failure_injected()) return hip_status(hipErrorLaunchFailure, where " (injected)"); \
+  } while (0)
 
 #define REQUIRE(cond, status, ...) \
   do {                              \
@@ -81,6 +96,7 @@ fp4_status fp4_quantize(const void* x, fp4_dtype xt, int64_t M, int64_t K, fp4_f
   }
   // an empty tensor only has a tensor scale (0) to produce, and only when computing it
   if (empty && !(fmt == FP4_NVFP4 && mode == FP4_SCALE_COMPUTE)) return ok();
+  INJECT_POINT("fp4_quantize");
   hipError_t e = fp4impl::launch_quantize(x, xt == FP4_BF16 ? fp4impl::DT_BF16 : fp4impl::DT_F32, M, K,
                                           fmt == FP4_MXFP4 ? fp4impl::FMT_MX : fp4impl::FMT_NV, hadamard,
                                           codes, scales, tensor_scale,
@@ -102,6 +118,7 @@ fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, const flo
   REQUIRE(fmt == FP4_MXFP4 || tensor_scale, FP4_E_NULL, "fp4_dequantize: NVFP4 needs tensor_scale");
   REQUIRE(aligned(codes, 16) && aligned(y, 16), FP4_E_ALIGN, "fp4_dequantize: codes and y must be 16-byte aligned");
   REQUIRE(aligned(scales, 4), FP4_E_ALIGN, "fp4_dequantize: scales must be 4-byte aligned");
+  INJECT_POINT("fp4_dequantize");
   hipError_t e = fp4impl::launch_dequantize(codes, scales, tensor_scale, M, K,
                                             fmt == FP4_MXFP4 ? fp4impl::FMT_MX : fp4impl::FMT_NV, inverse_hadamard,
                                             y, yt == FP4_BF16 ? fp4impl::DT_BF16 : fp4impl::DT_F32,
@@ -128,6 +145,7 @@ fp4_status fp4_residual_quantize(const void* x, int64_t M, int64_t K, const floa
     REQUIRE(aligned(x, 16) && aligned(codes, 16), FP4_E_ALIGN, "fp4_residual_quantize: x and codes must be 16-byte aligned");
     REQUIRE(!dbg_normed || aligned(dbg_normed, 16), FP4_E_ALIGN, "fp4_residual_quantize: dbg_normed misaligned");
   }
+  INJECT_POINT("fp4_residual_quantize");
   hipError_t e = fp4impl::launch_residual_quantize(reinterpret_cast<const uint16_t*>(x), M, K, gamma, eps, perm, S,
                                                    codes, scales, tensor_scale, mode == FP4_SCALE_COMPUTE,
                                                    dbg_normed, reinterpret_cast<hipStream_t>(stream));
@@ -152,6 +170,7 @@ fp4_status fp4_residual_quantize_mx(const void* x, int64_t M, int64_t K, const f
             "fp4_residual_quantize_mx: x and codes must be 16-byte aligned");
     REQUIRE(!dbg_normed || aligned(dbg_normed, 16), FP4_E_ALIGN, "fp4_residual_quantize_mx: dbg_normed misaligned");
   }
+  INJECT_POINT("fp4_residual_quantize_mx");
   hipError_t e = fp4impl::launch_residual_quantize_mx(reinterpret_cast<const uint16_t*>(x), M, K, gamma, eps, perm,
                                                       S, codes, scales, dbg_normed,
                                                       reinterpret_cast<hipStream_t>(stream));
@@ -170,6 +189,7 @@ fp4_status fp4_pack(const void* x, int64_t M, int64_t K, void* packed, float* db
   REQUIRE(x && packed, FP4_E_NULL, "fp4_pack: x and packed are required");
   REQUIRE(aligned(x, 16) && aligned(packed, 256), FP4_E_ALIGN, "fp4_pack: x must be 16-byte, packed 256-byte aligned");
   REQUIRE(!dbg_rotated || aligned(dbg_rotated, 16), FP4_E_ALIGN, "fp4_pack: dbg_rotated misaligned");
+  INJECT_POINT("fp4_pack");
   hipError_t e = fp4impl::launch_pack(reinterpret_cast<const uint16_t*>(x), M, K, reinterpret_cast<uint8_t*>(packed),
                                       dbg_rotated, reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "fp4_pack");
@@ -181,6 +201,7 @@ fp4_status fp4_unpack(const void* packed, int64_t M, int64_t K, void* y, void* s
   if (M == 0 || K == 0) return ok();
   REQUIRE(packed && y, FP4_E_NULL, "fp4_unpack: packed and y are required");
   REQUIRE(aligned(y, 16) && aligned(packed, 256), FP4_E_ALIGN, "fp4_unpack: y must be 16-byte, packed 256-byte aligned");
+  INJECT_POINT("fp4_unpack");
   hipError_t e = fp4impl::launch_unpack(reinterpret_cast<const uint8_t*>(packed), M, K, reinterpret_cast<uint16_t*>(y),
                                         reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "fp4_unpack");
@@ -198,6 +219,7 @@ fp4_status fp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
   REQUIRE(aligned(a_codes, 16) && aligned(b_codes, 16) && aligned(c, 16), FP4_E_ALIGN,
           "fp4_gemm: codes and c must be 16-byte aligned");
   REQUIRE(aligned(a_scales, 4) && aligned(b_scales, 4), FP4_E_ALIGN, "fp4_gemm: scales must be 4-byte aligned");
+  INJECT_POINT("fp4_gemm");
   hipError_t e = fp4impl::launch_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, c,
                                       ct == FP4_BF16 ? fp4impl::DT_BF16 : fp4impl::DT_F32,
                                       reinterpret_cast<hipStream_t>(stream));

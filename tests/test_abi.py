@@ -134,3 +134,30 @@ def test_missing_library_fails_loudly(monkeypatch):
         B.lib()
     with pytest.raises(RuntimeError, match="HIP library missing"):
         B.fp4_pack_bytes(4, 128)
+
+
+@needs_lib
+def test_injected_launch_failure_reports_hip_status(monkeypatch):
+    """FP4_FAULT_INJECT=launch: each entry point that passes validation reports FP4_E_HIP
+    through the library's HIP-status mapping, with a readable detail, and enqueues nothing
+    (the fake pointers below are never touched, so this runs without a GPU).  Validation
+    still decides first, and a clean environment makes the same call validate again."""
+    monkeypatch.setenv("FP4_FAULT_INJECT", "launch")
+    cases = [
+        ("fp4_quantize", (FAKE, 1, 4, 32, 1, 32, FAKE, FAKE, None, 0, None, None)),
+        ("fp4_dequantize", (FAKE, FAKE, None, 4, 64, 1, 0, FAKE, 0, None)),
+        ("fp4_residual_quantize", (FAKE, 4, 64, None, ctypes.c_float(1e-6), FAKE, 16, FAKE, FAKE, FAKE, 0,
+                                   None, None)),
+        ("fp4_residual_quantize_mx", (FAKE, 4, 64, None, ctypes.c_float(1e-6), FAKE, 32, FAKE, FAKE, None, None)),
+        ("fp4_pack", (FAKE, 4, 128, FAKE, None, None)),
+        ("fp4_unpack", (FAKE, 4, 128, FAKE, None)),
+        ("fp4_gemm", (FAKE, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, 1, None)),
+    ]
+    for name, args in cases:
+        s, msg = _status(name, *args)
+        assert s == 5, (name, s, msg)
+        assert msg.startswith(name) and "injected" in msg and len(msg) > len(name) + 12, msg
+        assert B.lib().fp4_status_str(s).decode() == "FP4_E_HIP"
+    assert _status("fp4_quantize", FAKE, 1, 4, 33, 1, 0, FAKE, FAKE, None, 0, None, None)[0] == 2
+    monkeypatch.setenv("FP4_FAULT_INJECT", "none")
+    assert _status("fp4_gemm", FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 1, None)[0] == 2

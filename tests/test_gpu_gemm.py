@@ -11,7 +11,8 @@ import torch
 
 import microscaled_fp4_quantization_block_amd as fp4
 from microscaled_fp4_quantization_block_amd import workloads as W
-from oracle import gemm, mxfp4
+from oracle import formats as F, gemm, mxfp4
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -63,8 +64,57 @@ def test_gemm_quantized_llm_operands():
     assert np.linalg.norm(_np(c) - exact) < 0.2 * np.linalg.norm(exact)
 
 
+def _check_h32_operand(xv, dbg, codes, scales, what):
+    """Hadamard-32 MXFP4 of float64 values xv against the GPU's rotated values (dbg, may be
+    None), E8M0 scales and packed codes, under the boundary rule: scales first, then the
+    codes given the GPU's scales.  Returns the count of boundary-tolerated code flips."""
+    ref = mxfp4.quantize(xv, hadamard=32)
+    if dbg is not None:
+        P.assert_values_close(dbg, ref["y"], 32, what=f"{what}: rotated values")
+    P.check_e8m0_scales(scales, ref["scales"], ref["amax"], what=f"{what}: E8M0 scales")
+    del ref
+    cond = mxfp4.quantize(xv, hadamard=32, block_scales=scales)
+    return P.check_e2m1_codes(F.unpack_nibbles(codes), cond["codes"], cond["elem_arg"], cond["y"], 32,
+                              what=f"{what}: codes")
+
+
+def test_w4a4_config_end_to_end():
+    """The W4A4 configuration as stated: the library's Hadamard-32 MXFP4 quantization of
+    bf16 N(0,1) activations A [8192, 8192] (seed 5) and of N(0, 0.02) weights [28672, 8192]
+    (seed 50), then the GEMM with bf16 output -- the launches the benchmark times.  A's
+    rotated values, scales and codes are checked on every row against the oracle, B on
+    every row that the 64 seeded 128 x 128 output tiles (seed 500) read, and those tiles
+    against the float64 product of the GPU's own operands."""
+    wl = W.WORKLOADS["w4a4_gemm"]
+    M, K = wl.shape
+    N, T = wl.extra["N"], wl.extra["tile"]
+    print(f"w4a4 config: A {M}x{K} seed {wl.seed}, W {N}x{K} seed {wl.extra['weight_seed']}", flush=True)
+    a_cpu = W.gemm_activations((M, K), wl.seed)
+    w_cpu = W.gemm_weights(N, K, wl.extra["weight_seed"], wl.extra["weight_std"])
+    dbg = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    a_codes, a_scales, _ = fp4.fp4_quantize(a_cpu.to(DEV), "mxfp4", 32, dbg_rotated=dbg)
+    w = w_cpu.to(DEV)
+    b_codes, b_scales, _ = fp4.fp4_quantize(w, "mxfp4", 32)
+    del w
+    c = fp4.fp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ac, asc, bc, bsc = _np(a_codes), _np(a_scales), _np(b_codes), _np(b_scales)
+    n = _check_h32_operand(W.values(a_cpu), _np(dbg), ac, asc, "A")
+    del dbg
+    tiles = W.gemm_tiles(M, N, T, wl.extra["tiles"], seed=wl.extra["tile_seed"])
+    assert len(tiles) == 64
+    cols = np.unique(np.concatenate([np.arange(c0, c0 + T) for _, c0 in tiles]))
+    n += _check_h32_operand(W.values(w_cpu[torch.from_numpy(cols)]), None, bc[cols], bsc[cols], "B")
+    print(f"  boundary-tolerated code differences: {n}; checking 64 tiles", flush=True)
+    for (r0, c0) in tiles:
+        tile = W.values(c[r0:r0 + T, c0:c0 + T].cpu())
+        ref = gemm.tile(ac, asc, bc, bsc, np.arange(r0, r0 + T), np.arange(c0, c0 + T))
+        _assert_gemm_close(tile, ref, True)
+
+
 def test_gemm_config_full_size_sampled_tiles():
-    """8192 x 28672 x 8192 (the 70B-class MLP projection shape), 64 seeded 128 x 128 tiles."""
+    """8192 x 28672 x 8192 (the 70B-class MLP projection shape) on uniform random code
+    bytes (every element value and sign), 64 seeded 128 x 128 tiles."""
     M, N, K = 8192, 28672, 8192
     print("gemm 8192x28672x8192 bf16, 64 tiles", flush=True)
     a, sa = W.random_mxfp4_operand(M, K, seed=5, exp_lo=123, exp_hi=127)

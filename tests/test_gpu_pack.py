@@ -53,11 +53,10 @@ def test_pack_small(shape):
 
 
 def test_pack_config_full_size():
-    """bf16 8192 x 8192 Student-t(4), sampled rows."""
+    """bf16 8192 x 8192 Student-t(4), every row."""
     print("pack 8192x8192 Student-t(4) seed 3", flush=True)
     x = W.student_t_input()
-    rows = W.seeded_rows(8192, 48, 30)
-    n = _check_pack(x, rows)
+    n = _check_pack(x)
     print(f"  boundary-tolerated code differences: {n}", flush=True)
 
 
