@@ -4,20 +4,31 @@ Default workload (one step = the whole path on one batch):
   Hadamard-32 + MXFP4 quantization of bf16 activations A [8192, 8192] (fp4_quantize), then
   the W4A4 MXFP4 GEMM C = A W^T against offline-rotated MXFP4 weights W [28672, 8192]
   (fp4_gemm, bf16 out).  Inputs are seeded synthetic stand-ins (N(0,1) activations,
-  N(0, 0.02) weights) already resident in HBM when timing starts.
+  N(0, 0.02) weights) already resident in HBM when timing starts; the steps cycle through
+  1 GiB of activation batches so the quantization reads HBM, not the Infinity Cache.
 
 Prints one JSON line: whole-step throughput in TFLOP/s (2 M N K per step), the roofline
 of the dominant kernel (the GEMM, against the 10.1 PFLOP/s dense FP4 MFMA peak) and of the
 quantization kernel (against 8 TB/s HBM), both from HIP events recorded around each launch
-inside the timed loop, and the CPU oracle timed on a bounded sample of the same workload.
+inside the timed loop, and the CPU oracle timed on a bounded sample of the same workload
+(all cores and one thread).
+
+Before the warmup steps every workload repeats its step untimed for --settle seconds
+(default 1): the shader clock needs about half a second of load to leave its idle level
+and settle where the board's power limit holds it, so a few warmup steps alone would time
+the ramp.  The JSON line reports the settle phase.
 
 Other workloads (--workload) time one kernel each against the HBM roofline, rotating
 through >= 1 GiB of buffer sets so the 256 MB Infinity Cache cannot serve them.
 `--workload hbm_copy` times a plain 1 GiB device-to-device copy: the reference point
-that scales the HBM byte counters of the kernels above.
+that scales the HBM byte counters of the kernels above.  `--workload hbm_read` and
+`--workload mfma_peak` run the roofline probes (libfp4probe.so): the read-only HBM
+ceiling at a given working-set size and the register-only FP4 MFMA rate.
 """
 import argparse
+import hashlib
 import json
+import multiprocessing
 import os
 import sys
 import time
@@ -38,16 +49,54 @@ DEV = "cuda:0"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
+CSRC = os.path.join(ROOT, "microscaled_fp4_quantization_block_amd", "csrc")
+
+
+def source_sha(files):
+    """SHA-256 (first 16 hex digits) of the listed kernel sources, in order."""
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def _traffic(kernel_key):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if one exists."""
+    """Calibrated HBM bytes per launch from the committed counter summary
+    (profiles/traffic.json), or None when there is none or when the kernel's sources have
+    changed since the counters were taken (the entry records their hash)."""
     path = os.path.join(PROFILE_DIR, "traffic.json")
-    if not os.path.exists(path):
-        return None
     try:
         with open(path) as f:
-            return json.load(f).get(kernel_key)
+            entry = json.load(f).get(kernel_key)
     except (OSError, ValueError):
         return None
+    if not isinstance(entry, dict) or "bytes" not in entry:
+        return None
+    try:
+        if source_sha(entry["sources"]) != entry["source_sha"]:
+            return None
+    except (KeyError, OSError):
+        return None
+    return entry["bytes"]
+
+
+def settle(fn, seconds):
+    """Untimed: repeat fn until `seconds` of wall time have passed, synchronising every few
+    calls.  The shader clock needs about half a second of load to leave its idle state and
+    reach the level the power limit sets; a few warmup steps alone would time the ramp."""
+    if seconds <= 0:
+        return {"seconds": 0.0, "calls": 0}
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return {"seconds": el, "calls": n}
 
 
 class Timer:
@@ -71,50 +120,128 @@ class Timer:
 
 
 # ----------------------------------------------------------------------------- CPU baseline
+#
+# The oracle as it stands (float64 numpy, oracle/) timed on the host's cores on a bounded
+# sample of the workload: once on one thread, once on every core the process may use.
+# Memory-bound workloads run the oracle on row chunks in spawned worker processes (one
+# BLAS thread each; they never touch the GPU); the W4A4 step, whose time is the float64
+# product, runs in-process on all BLAS threads.
 
-def cpu_baseline_gemm(a_bf16, w_bf16, rows=None, cols=None):
-    """Oracle (float64 numpy) on a bounded sample of the step, by default all of it:
-    Hadamard-32 MXFP4 of `rows` activation rows, then their GEMM against `cols` weight rows
-    quantized the same way (untimed setup).  Throughput in the step's unit:
-    2 rows cols K / time."""
-    rows = a_bf16.shape[0] if rows is None else rows
-    cols = w_bf16.shape[0] if cols is None else cols
-    from threadpoolctl import threadpool_info
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:          # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _oracle_op(name, data):
+    """One oracle evaluation of workload op `name` on a row chunk `data` (a tuple)."""
+    from oracle import arcquant, dualscale, mxfp4, nvfp4
+    from oracle.hadamard import two_level_128
+    if name == "mxfp4_h32_quant":
+        mxfp4.quantize(data[0], hadamard=32)
+    elif name == "mxfp4_h32_dequant":
+        mxfp4.dequantize(data[0], data[1], inverse_hadamard=32)
+    elif name == "dualscale_pack_quant":
+        dualscale.pack_values(data[0])
+    elif name == "dualscale_pack_dequant":
+        two_level_128(dualscale.dequantized(*data))
+    elif name == "arcquant_quant":
+        arcquant.quantize(data[0], data[1], data[2], tensor_scale_value=data[3])
+    elif name == "nvfp4_roundtrip_quant":
+        q = nvfp4.quantize(data[0])
+        nvfp4.dequantize(q["packed"], q["scales"], q["tensor_scale"])
+    else:
+        raise ValueError(name)
+
+
+def _timed_oracle_chunk(job):
+    from threadpoolctl import threadpool_limits
+    name, data = job
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        _oracle_op(name, data)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline_rows(name, chunk, rows_total, bytes_per_row, what, target_s=3.0, max_chunk_rows=None):
+    """Oracle throughput in GB/s over the same algorithmic bytes per row as the GPU line.
+
+    chunk(lo, hi) returns the oracle's input tuple for rows [lo, hi).  One thread: a
+    sample sized to about `target_s`.  All cores: one chunk of the same size per core,
+    each in its own process, timed from the first submission to the last result."""
+    probe_rows = max(1, min(rows_total, 8))
+    t = _timed_oracle_chunk((name, chunk(0, probe_rows)))
+    rows1 = int(min(rows_total, max(probe_rows, target_s * probe_rows / max(t, 1e-6))))
+    if max_chunk_rows:
+        rows1 = min(rows1, max_chunk_rows)
+    t1 = _timed_oracle_chunk((name, chunk(0, rows1)))
+    one = {"value": rows1 * bytes_per_row / t1 / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "seconds": t1, "sample": f"{what}: {rows1} rows on one thread"}
+    n = host_cores()
+    per = max(1, min(rows1, rows_total // n))
+    span = rows_total - per + 1
+    jobs = [(name, chunk((k * per) % span, (k * per) % span + per)) for k in range(n)]
+    ctx = multiprocessing.get_context("spawn")
+    with ctx.Pool(n) as pool:
+        pool.map(_timed_oracle_chunk, [(name, chunk(0, 1))] * n)          # workers started and warm
+        t0 = time.perf_counter()
+        pool.map(_timed_oracle_chunk, jobs, chunksize=1)
+        tn = time.perf_counter() - t0
+    return {"value": n * per * bytes_per_row / tn / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+            "seconds": tn, "sample": f"{what}: {n} chunks of {per} rows, one process per core",
+            "one_thread": one}
+
+
+def cpu_baseline_gemm(a_bf16, w_bf16, rows, rows1=256):
+    """Oracle on a bounded sample of the W4A4 step: Hadamard-32 MXFP4 of `rows` activation
+    rows, then their float64 GEMM against every weight row quantized the same way (the
+    weights are quantized untimed, as they are offline on the GPU side).  Throughput in the
+    step's unit, 2 rows N K / time: on all BLAS threads, and on one thread for `rows1`."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import gemm, mxfp4
-    K = a_bf16.shape[1]
-    a = W.values(a_bf16[:rows])
-    w = W.values(w_bf16[:cols])
-    qw = mxfp4.quantize(w, hadamard=32)                       # offline weights (untimed)
-    t0 = time.perf_counter()
-    qa = mxfp4.quantize(a, hadamard=32)
-    c = gemm.tile(qa["packed"], qa["scales"], qw["packed"], qw["scales"], np.arange(rows), np.arange(cols))
-    dt = time.perf_counter() - t0
-    assert c.shape == (rows, cols)
+    K, N = a_bf16.shape[1], w_bf16.shape[0]
+    w = W.values(w_bf16)
+    qw = mxfp4.quantize(w, hadamard=32)
+    del w
+
+    def run(r):
+        a = W.values(a_bf16[:r])
+        t0 = time.perf_counter()
+        qa = mxfp4.quantize(a, hadamard=32)
+        c = gemm.tile(qa["packed"], qa["scales"], qw["packed"], qw["scales"], np.arange(r), np.arange(N))
+        dt = time.perf_counter() - t0
+        assert c.shape == (r, N)
+        return dt
+
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": 2.0 * rows * cols * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"Hadamard-32 MXFP4 quantization of {rows} activation rows + float64 GEMM against "
-                      f"{cols} oracle-quantized weight rows, K={K} ({rows}x{cols} of the "
-                      f"{a_bf16.shape[0]}x{w_bf16.shape[0]} output)"}
-
-
-def cpu_baseline_bytes(fn, nbytes, what):
-    t0 = time.perf_counter()
-    fn()
-    dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "seconds": dt,
-            "sample": what}
+    dt = run(rows)
+    with threadpool_limits(1):
+        dt1 = run(rows1)
+    what = (f"Hadamard-32 MXFP4 quantization of {{r}} activation rows + float64 GEMM against all {N} "
+            f"oracle-quantized weight rows, K={K} ({{r}}x{N} of the {a_bf16.shape[0]}x{N} output)")
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt, "sample": what.format(r=rows) + f", {threads} BLAS threads",
+            "one_thread": {"value": 2.0 * rows1 * N * K / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                           "kind": "oracle", "seconds": dt1, "sample": what.format(r=rows1) + ", one thread"}}
 
 
 # ----------------------------------------------------------------------------- workloads
 
 def run_w4a4_gemm(args):
+    """The whole hot path per step: Hadamard-32 MXFP4 quantization of one activation batch
+    A, then the W4A4 GEMM against the pre-quantized weights.  Steps cycle through
+    activation batches totalling >= 1 GiB (A is 128 MiB), so every quantization reads its
+    input from HBM rather than from the 256 MB Infinity Cache; the batches are row
+    rotations of the seeded A, the same values in another order."""
     wl = W.WORKLOADS["w4a4_gemm"]
     M, K = wl.shape
     N = wl.extra["N"]
     a_cpu = W.gemm_activations((M, K), wl.seed)
     w_cpu = W.gemm_weights(N, K, wl.extra["weight_seed"], wl.extra["weight_std"])
-    a = a_cpu.to(DEV)
+    a0 = a_cpu.to(DEV)
+    n_a = max(2, -(-(1 << 30) // (M * K * 2)))
+    a_sets = [a0] + [torch.roll(a0, shifts=977 * i, dims=0) for i in range(1, n_a)]
     w = w_cpu.to(DEV)
     # offline: rotate + quantize the weights (not part of the step)
     b_codes, b_scales, _ = fp4.fp4_quantize(w, "mxfp4", 32)
@@ -122,8 +249,11 @@ def run_w4a4_gemm(args):
     a_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
     a_scales = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    it = [0]
 
     def step(tq=None, tg=None):
+        a = a_sets[it[0] % n_a]
+        it[0] += 1
         s = tq.start() if tq else None
         fp4.fp4_quantize(a, "mxfp4", 32, codes=a_codes, scales=a_scales)
         if tq:
@@ -133,6 +263,7 @@ def run_w4a4_gemm(args):
         if tg:
             tg.stop(s)
 
+    settled = settle(step, args.settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -155,7 +286,8 @@ def run_w4a4_gemm(args):
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no model weights or datasets)",
         "config": {"workload": "w4a4_gemm: Hadamard-32 MXFP4 quantization of A bf16 8192x8192 + "
                                "W4A4 MXFP4 GEMM against rotated MXFP4 weights 28672x8192, bf16 out",
-                   "M": M, "N": N, "K": K, "parallelism": "single GPU"},
+                   "M": M, "N": N, "K": K, "activation_batches": n_a, "parallelism": "single GPU"},
+        "settle": settled,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / FP4_PEAK_TFLOPS, "traffic": _traffic("gemm_w4a4"),
                      "kernel": "k_gemm", "kernel_ms": gemm_ms, "flop_per_launch": flops},
@@ -165,7 +297,7 @@ def run_w4a4_gemm(args):
                               "bytes_per_launch": quant_bytes},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline_gemm(a_cpu, w_cpu)
+        out["cpu_baseline"] = cpu_baseline_gemm(a_cpu, w_cpu, rows=M)
     return out
 
 
@@ -203,6 +335,7 @@ def run_arcquant_gemm(args):
 
     res = {}
     for name, s_, a, b in (("augmented", S, a_aug, b_aug), ("base", 0, a_base, b_base)):
+        settle(lambda: step(s_, a, b), args.settle)
         for _ in range(args.warmup):
             step(s_, a, b)
         torch.cuda.synchronize()
@@ -307,6 +440,7 @@ def run_hbm_copy(args):
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(7)
     dst = torch.empty_like(src)
+    settled = settle(lambda: dst.copy_(src), args.settle)
     for _ in range(args.warmup):
         dst.copy_(src)
     torch.cuda.synchronize()
@@ -322,18 +456,21 @@ def run_hbm_copy(args):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": kms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "hbm_copy: 1 GiB device-to-device copy (counter calibration)"},
+            "settle": settled,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "torch copy",
                          "kernel_ms": kms, "bytes_per_launch": 2 * n}}
 
 
 def _memory_case(name, op):
-    """(make, launch, bytes per launch, kernel label) of one memory-bound workload op."""
+    """(make, launch, bytes per launch, kernel label, cpu) of one memory-bound workload op;
+    cpu = (oracle op name, chunk(lo, hi) -> oracle input of rows [lo, hi), rows, what)."""
     wl = W.WORKLOADS[name]
     M, K = wl.shape
     if name == "mxfp4_h32":
         x_cpu = W.mxfp4_h32_input(wl.shape, wl.seed)
         nbytes = M * K * 2 + M * K // 2 + M * K // 32
+        xv = W.values(x_cpu)
         if op == "quant":
             def make():
                 return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
@@ -341,43 +478,59 @@ def _memory_case(name, op):
 
             def launch(s):
                 fp4.fp4_quantize(s[0], "mxfp4", 32, codes=s[1], scales=s[2])
-            return make, launch, nbytes, "k_quant_mx<bf16,32>"
+            cpu = ("mxfp4_h32_quant", lambda lo, hi: (xv[lo:hi],), M, "oracle mxfp4.quantize(hadamard=32)")
+            return make, launch, nbytes, "k_quant_mx<bf16,32>", cpu
         codes, scales, _ = fp4.fp4_quantize(x_cpu.to(DEV), "mxfp4", 32)
+        cn, sn = codes.cpu().numpy(), scales.cpu().numpy()
 
         def make():
             return (codes.clone(), scales.clone(), torch.empty((M, K), dtype=torch.bfloat16, device=DEV))
 
         def launch(s):
             fp4.fp4_dequantize(s[0], s[1], None, "mxfp4", 32, y=s[2])
-        return make, launch, nbytes, "k_dequant<MX,32,bf16> (inverse H32)"
+        cpu = ("mxfp4_h32_dequant", lambda lo, hi: (cn[lo:hi], sn[lo:hi]), M,
+               "oracle mxfp4.dequantize(inverse_hadamard=32)")
+        return make, launch, nbytes, "k_dequant<MX,32,bf16> (inverse H32)", cpu
     if name == "dualscale_pack":
         x_cpu = W.student_t_input(wl.shape, wl.seed)
         nbytes = M * K * 2 + M * K // 2 + M * K // 16 + 4 * M * K // 128
         nb = fp4.fp4_pack_bytes(M, K)
         if op == "quant":
+            xv = W.values(x_cpu[:1024])
+
             def make():
                 return (x_cpu.to(DEV), torch.empty(nb, dtype=torch.uint8, device=DEV))
 
             def launch(s):
                 fp4.fp4_pack(s[0], packed=s[1])
-            return make, launch, nbytes, "k_pack"
+            cpu = ("dualscale_pack_quant", lambda lo, hi: (xv[lo:hi],), 1024,
+                   "oracle dualscale.pack_values (rows of the first 1024)")
+            return make, launch, nbytes, "k_pack", cpu
         packed = fp4.fp4_pack(x_cpu.to(DEV))
+        from oracle import dualscale as _ds
+        codes, sm, sg = _ds.split(packed.cpu().numpy(), M, K)
+        codes, sm, sg = codes[:1024], sm[:1024], sg[:1024]
 
         def make():
             return (packed.clone(), torch.empty((M, K), dtype=torch.bfloat16, device=DEV))
 
         def launch(s):
             fp4.fp4_unpack(s[0], M, K, y=s[1])
-        return make, launch, nbytes, "k_unpack"
+        cpu = ("dualscale_pack_dequant", lambda lo, hi: (codes[lo:hi], sm[lo:hi], sg[lo:hi]), 1024,
+               "oracle two-level FWHT of dualscale.dequantized (rows of the first 1024)")
+        return make, launch, nbytes, "k_unpack", cpu
     if name == "arcquant":
         if op != "quant":
             raise SystemExit("arcquant has no inverse op")
         x_cpu = W.arcquant_input(wl.shape, wl.seed)
         S = wl.extra["S"]
-        perm = torch.from_numpy(W.calibration_order(x_cpu)).to(DEV)
+        perm_np = W.calibration_order(x_cpu)
+        perm = torch.from_numpy(perm_np).to(DEV)
         ts = torch.zeros(1, dtype=torch.float32, device=DEV)
         fp4.fp4_residual_quantize(x_cpu.to(DEV), perm, S, tensor_scale=ts)        # calibrate once
         nbytes = M * K * 2 + K * 4 + M * (K + S) // 2 + M * (K + S) // 16 + 4
+        xv = W.values(x_cpu)
+        st = np.float32(ts.cpu().numpy()[0])
 
         def make():
             return (x_cpu.to(DEV), torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=DEV),
@@ -385,12 +538,15 @@ def _memory_case(name, op):
 
         def launch(s):
             fp4.fp4_residual_quantize(s[0], perm, S, codes=s[1], scales=s[2], tensor_scale=ts, mode="given")
-        return make, launch, nbytes, "k_arcquant<false> (static tensor scale)"
+        cpu = ("arcquant_quant", lambda lo, hi: (xv[lo:hi], perm_np, S, st), M,
+               "oracle arcquant.quantize with the calibrated tensor scale")
+        return make, launch, nbytes, "k_arcquant<NVFP4> (static tensor scale)", cpu
     if name == "nvfp4_roundtrip":
         if op != "quant":
             raise SystemExit("nvfp4_roundtrip times quantize + dequantize together")
         x_cpu = W.nvfp4_roundtrip_input(wl.shape, wl.seed)
         nbytes = 2 * (M * K * 4 + M * K // 2 + M * K // 16 + 4)
+        xv = W.values(x_cpu)
 
         def make():
             return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
@@ -401,7 +557,9 @@ def _memory_case(name, op):
         def launch(s):
             fp4.fp4_quantize(s[0], "nvfp4", 0, codes=s[1], scales=s[2], tensor_scale=s[3])
             fp4.fp4_dequantize(s[1], s[2], s[3], "nvfp4", 0, y=s[4])
-        return make, launch, nbytes, "NVFP4 round trip (amax, quantize, dequantize kernels)"
+        cpu = ("nvfp4_roundtrip_quant", lambda lo, hi: (xv[lo:hi],), M,
+               "oracle nvfp4.quantize + nvfp4.dequantize (the chunk's own tensor scale)")
+        return make, launch, nbytes, "NVFP4 round trip (amax, quantize, dequantize kernels)", cpu
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -411,15 +569,22 @@ def run_memory_workload(args):
     bracketed by one HIP event pair on the replay stream."""
     name, op = args.workload, args.op
     wl = W.WORKLOADS[name]
-    make, launch, nbytes, kernel = _memory_case(name, op)
+    make, launch, nbytes, kernel, cpu = _memory_case(name, op)
     sets = _rotating(make, nbytes)
-    for i in range(args.warmup):
-        launch(sets[i % len(sets)])
+    i = [0]
+
+    def one():
+        launch(sets[i[0] % len(sets)])
+        i[0] += 1
+
+    settled = settle(one, args.settle)
+    for _ in range(args.warmup):
+        one()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(args.steps):
-            launch(sets[i % len(sets)])
+        for k in range(args.steps):
+            launch(sets[k % len(sets)])
     g.replay()                                   # untimed: first replay uploads the graph
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -437,11 +602,121 @@ def run_memory_workload(args):
            "dtype": "fp32 arithmetic; bf16/fp32 in, e2m1 + e4m3/e8m0 out" if op == "quant"
            else "fp32 arithmetic; e2m1 + e4m3/e8m0 in, bf16/fp32 out",
            "data": "synthetic", "config": {"workload": f"{name} ({op}): {wl.description}"},
+           "settle": settled,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(f"{name}_{op}"), "kernel": kernel,
                         "kernel_ms": kms, "bytes_per_launch": nbytes, "buffer_sets": len(sets),
                         "timing": "one HIP event pair around a graph replay of `steps` launches"}}
+    if not args.no_cpu:
+        oname, chunk, rows, what = cpu
+        out["cpu_baseline"] = cpu_baseline_rows(oname, chunk, rows, nbytes / wl.shape[0], what)
     return out
+
+
+# ----------------------------------------------------------------------------- roofline probes
+
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "microscaled_fp4_quantization_block_amd", "libfp4probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"probe library missing: {path} (run the build)")
+    L = ctypes.CDLL(path)
+    L.fp4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.fp4probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
+def _graph_time(launch, steps):
+    """Mean ms per launch: `steps` launches (launch(k)) captured into one HIP graph, one
+    untimed replay, then one replay between a HIP event pair on the replay stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(steps):
+            launch(k)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_hbm_read(args):
+    """Read-only HBM ceiling: coalesced 16-byte loads over buffers of `--bytes` each,
+    rotating through >= 1 GiB of them, one launch per buffer (graph-replayed)."""
+    import ctypes
+    L = _probe_lib()
+    nbytes = args.bytes
+    sets = _rotating(lambda: torch.empty(nbytes, dtype=torch.uint8, device=DEV).fill_(3), nbytes)
+    blocks = 256 * 8
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=DEV)
+
+    def launch(k):
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if L.fp4probe_hbm_read(ctypes.c_void_p(sets[k % len(sets)].data_ptr()), nbytes,
+                               ctypes.c_void_p(sink.data_ptr()), blocks, st) != 0:
+            raise RuntimeError("fp4probe_hbm_read failed")
+
+    i = [0]
+
+    def one():
+        launch(i[0])
+        i[0] += 1
+    settled = settle(one, args.settle)
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    kms = _graph_time(launch, args.steps)
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    return {"metric": "HBM read GB/s (roofline probe)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": kms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": f"hbm_read: {nbytes} bytes per launch, {len(sets)} rotating buffers"},
+            "settle": settled,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_hbm_read",
+                         "kernel_ms": kms, "bytes_per_launch": nbytes,
+                         "timing": "one HIP event pair around a graph replay of `steps` launches"}}
+
+
+def run_mfma_peak(args):
+    """Register-only scaled FP4 MFMA loop (v_mfma_scale_f32_32x32x64_f8f6f4), eight waves
+    per CU shaped like the GEMM's, with constant (--mode 0), fixed random (1) or changing
+    (2) operand bytes: the sustained FP4 rate the power limit allows for each."""
+    import ctypes
+    L = _probe_lib()
+    blocks, iters = 256 * 4, args.iters
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=DEV)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    flop = float(blocks) * 8 * iters * 8 * 131072
+
+    def one():
+        if L.fp4probe_mfma_loop(iters, args.mode, blocks, ctypes.c_void_p(sink.data_ptr()), st) != 0:
+            raise RuntimeError("fp4probe_mfma_loop failed")
+    settled = settle(one, args.settle)
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t = Timer()
+    for _ in range(args.steps):
+        s = t.start()
+        one()
+        t.stop(s)
+    torch.cuda.synchronize()
+    kms = t.mean_ms()
+    tf = flop / (kms * 1e-3) / 1e12
+    mode = {0: "constant", 1: "fixed random", 2: "changing random"}[args.mode]
+    return {"metric": "register-only FP4 MFMA TFLOP/s (roofline probe)", "value": tf, "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": kms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1/e8m0 (fp32 accumulate)", "data": "synthetic",
+            "config": {"workload": f"mfma_peak: {blocks} workgroups x 8 waves x {iters} iterations x 8 MFMA, "
+                                   f"{mode} operands"},
+            "settle": settled,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP4_PEAK_TFLOPS, "traffic": None, "kernel": "k_mfma_loop",
+                         "kernel_ms": kms, "flop_per_launch": flop}}
 
 
 def main():
@@ -449,9 +724,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="w4a4_gemm", choices=sorted(W.WORKLOADS) + ["hbm_copy", "format_study"])
+    ap.add_argument("--workload", default="w4a4_gemm",
+                    choices=sorted(W.WORKLOADS) + ["hbm_copy", "hbm_read", "mfma_peak", "format_study"])
     ap.add_argument("--op", default="quant", choices=["quant", "dequant"],
                     help="memory workloads: time the forward op (quantize / pack) or its inverse")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed repetitions before the warmup steps, so the shader clock "
+                         "has left its idle state (0 disables)")
+    ap.add_argument("--bytes", type=int, default=1 << 30, help="hbm_read: bytes per launch")
+    ap.add_argument("--mode", type=int, default=2, choices=[0, 1, 2], help="mfma_peak: operand bytes")
+    ap.add_argument("--iters", type=int, default=20000, help="mfma_peak: loop iterations per wave")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -461,16 +743,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     fp4.lib()                                   # fail loudly if the HIP library is missing
-    if args.workload == "w4a4_gemm":
-        out = run_w4a4_gemm(args)
-    elif args.workload == "arcquant_gemm":
-        out = run_arcquant_gemm(args)
-    elif args.workload == "format_study":
-        out = run_format_study(args)
-    elif args.workload == "hbm_copy":
-        out = run_hbm_copy(args)
-    else:
-        out = run_memory_workload(args)
+    runners = {"w4a4_gemm": run_w4a4_gemm, "arcquant_gemm": run_arcquant_gemm, "format_study": run_format_study,
+               "hbm_copy": run_hbm_copy, "hbm_read": run_hbm_read, "mfma_peak": run_mfma_peak}
+    out = runners.get(args.workload, run_memory_workload)(args)
     print(json.dumps(out), flush=True)
 
 

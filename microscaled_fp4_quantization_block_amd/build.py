@@ -1,8 +1,9 @@
-"""Build libfp4.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+"""Build libfp4.so (the HIP kernels + C ABI) and libfp4probe.so (the roofline probes)
+in-tree for gfx950 with hipcc.
 
 Usage: python -m microscaled_fp4_quantization_block_amd.build   (or build() from Python)
-Every call recompiles.  Objects go to _build/ (git-ignored); the shared library lands
-next to this file, where the Python binding loads it.
+Every call recompiles.  Objects go to _build/ (git-ignored); the shared libraries land
+next to this file, where the Python binding and the benchmark load them.
 """
 import os
 import subprocess
@@ -15,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4.so")
 SOURCES = ["api.cpp", "quant.hip", "pack.hip", "arcquant.hip", "gemm.hip"]
+PROBE_LIB = os.path.join(PKG, "libfp4probe.so")
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 
@@ -43,18 +46,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

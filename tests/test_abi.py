@@ -161,3 +161,23 @@ def test_injected_launch_failure_reports_hip_status(monkeypatch):
     assert _status("fp4_quantize", FAKE, 1, 4, 33, 1, 0, FAKE, FAKE, None, 0, None, None)[0] == 2
     monkeypatch.setenv("FP4_FAULT_INJECT", "none")
     assert _status("fp4_gemm", FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 1, None)[0] == 2
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "fp4_probe.h")
+PROBE_LIB = os.path.join(os.path.dirname(B.library_path()), "libfp4probe.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBE_LIB), reason="libfp4probe.so not built")
+def test_probe_library_exports_its_header_and_rejects_bad_arguments():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fp4probe_[a-z_]+)\s*\(", text)))
+    assert names == ["fp4probe_hbm_read", "fp4probe_mfma_loop"]
+    L = ctypes.CDLL(PROBE_LIB)
+    for n in names:
+        assert hasattr(L, n)
+    L.fp4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.fp4probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.fp4probe_hbm_read(None, 1024, FAKE, 4, None) == 1
+    assert L.fp4probe_hbm_read(FAKE, 1000, FAKE, 4, None) == 1      # not a multiple of 16
+    assert L.fp4probe_mfma_loop(10, 3, 4, FAKE, None) == 1            # unknown operand mode
+    assert L.fp4probe_mfma_loop(10, 0, 0, FAKE, None) == 1
