@@ -55,13 +55,18 @@ typedef enum { FP4_SCALE_COMPUTE = 0, FP4_SCALE_GIVEN = 1 } fp4_scale_mode;
  *   fmt          FP4_NVFP4: E4M3 scale per 16 + one fp32 tensor scale
  *                FP4_MXFP4: E8M0 scale per 32
  *   hadamard     0 (none), 16 or 32: orthonormal Sylvester H_n applied to every
- *                contiguous n-block of a row before quantization
+ *                contiguous n-block of a row before quantization; 128: the two-level
+ *                transform of every contiguous 128-group (H_16 inside each 16-element
+ *                micro-group, then H_8 across the group's 8 micro-groups; equal to the
+ *                Sylvester H_128), after the FP4Quant abstract (paperdot.bitmofang.com:
+ *                hybrid two-level FWHT)
  *   codes        [M][K/2] output bytes
  *   scales       [M][K/16] (NVFP4) or [M][K/32] (MXFP4) output bytes
  *   tensor_scale NVFP4 only, one fp32: written (FP4_SCALE_COMPUTE: fl32(amax/2688) of the
  *                rotated tensor) or read (FP4_SCALE_GIVEN).  Must be NULL for MXFP4.
  *   dbg_rotated  optional [M][K] fp32 output of the rotated values (NULL = not written)
- * Shapes: M >= 0, K >= 0, K % 32 == 0.  M*K == 0 is a no-op (NVFP4 COMPUTE writes 0).
+ * Shapes: M >= 0, K >= 0, K % 32 == 0 (K % 128 == 0 with hadamard 128).  M*K == 0 is a
+ * no-op (NVFP4 COMPUTE writes 0).
  * Unrotated codes and scales are the exact round-to-nearest-even decisions of x/scale.
  * Rotated input is quantized from its binary32 rotated values with binary32 scale and
  * element arithmetic: a decision can differ from the exact one only where the real
@@ -76,9 +81,9 @@ fp4_status fp4_quantize(const void* x, fp4_dtype xt, int64_t M, int64_t K, fp4_f
  *
  * Mirror of fp4_quantize (same sources).  y[m][k] = fl32(V(code) * s_b * s_t) for
  * NVFP4 or V(code) * 2^(e-127) for MXFP4, then H_n applied per n-block when
- * inverse_hadamard is 16 or 32 (H_n is its own inverse), then rounded to yt
- * (bf16: nearest-even from the fp32 value).  tensor_scale: NVFP4 only (1 fp32, read).
- * Shapes as fp4_quantize.
+ * inverse_hadamard is 16 or 32, or the two-level 128 transform per 128-group when it is
+ * 128 (each is its own inverse), then rounded to yt (bf16: nearest-even from the fp32
+ * value).  tensor_scale: NVFP4 only (1 fp32, read).  Shapes as fp4_quantize.
  */
 fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                           int64_t M, int64_t K, fp4_format fmt, int inverse_hadamard,

@@ -76,11 +76,13 @@ fp4_status fp4_quantize(const void* x, fp4_dtype xt, int64_t M, int64_t K, fp4_f
                         float* dbg_rotated, void* stream) {
   REQUIRE(fmt == FP4_NVFP4 || fmt == FP4_MXFP4, FP4_E_UNSUPPORTED, "fp4_quantize: unknown format %d", (int)fmt);
   REQUIRE(xt == FP4_F32 || xt == FP4_BF16, FP4_E_UNSUPPORTED, "fp4_quantize: unknown input dtype %d", (int)xt);
-  REQUIRE(hadamard == 0 || hadamard == 16 || hadamard == 32, FP4_E_UNSUPPORTED,
-          "fp4_quantize: hadamard must be 0, 16 or 32 (got %d)", hadamard);
+  REQUIRE(hadamard == 0 || hadamard == 16 || hadamard == 32 || hadamard == 128, FP4_E_UNSUPPORTED,
+          "fp4_quantize: hadamard must be 0, 16, 32 or 128 (got %d)", hadamard);
   REQUIRE(mode == FP4_SCALE_COMPUTE || mode == FP4_SCALE_GIVEN, FP4_E_UNSUPPORTED, "fp4_quantize: bad scale mode");
   REQUIRE(M >= 0 && K >= 0, FP4_E_SHAPE, "fp4_quantize: negative size M=%lld K=%lld", (long long)M, (long long)K);
   REQUIRE(K % 32 == 0, FP4_E_SHAPE, "fp4_quantize: K=%lld is not a multiple of 32", (long long)K);
+  REQUIRE(hadamard != 128 || K % 128 == 0, FP4_E_SHAPE,
+          "fp4_quantize: the two-level 128 rotation needs K %% 128 == 0 (K=%lld)", (long long)K);
   const bool empty = (M == 0 || K == 0);
   if (fmt == FP4_NVFP4) {
     REQUIRE(tensor_scale != nullptr, FP4_E_NULL, "fp4_quantize: NVFP4 needs tensor_scale");
@@ -109,10 +111,12 @@ fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t K, fp4_format fmt, int inverse_hadamard, void* y, fp4_dtype yt, void* stream) {
   REQUIRE(fmt == FP4_NVFP4 || fmt == FP4_MXFP4, FP4_E_UNSUPPORTED, "fp4_dequantize: unknown format %d", (int)fmt);
   REQUIRE(yt == FP4_F32 || yt == FP4_BF16, FP4_E_UNSUPPORTED, "fp4_dequantize: unknown output dtype");
-  REQUIRE(inverse_hadamard == 0 || inverse_hadamard == 16 || inverse_hadamard == 32, FP4_E_UNSUPPORTED,
-          "fp4_dequantize: inverse_hadamard must be 0, 16 or 32");
+  REQUIRE(inverse_hadamard == 0 || inverse_hadamard == 16 || inverse_hadamard == 32 || inverse_hadamard == 128,
+          FP4_E_UNSUPPORTED, "fp4_dequantize: inverse_hadamard must be 0, 16, 32 or 128");
   REQUIRE(M >= 0 && K >= 0, FP4_E_SHAPE, "fp4_dequantize: negative size");
   REQUIRE(K % 32 == 0, FP4_E_SHAPE, "fp4_dequantize: K=%lld is not a multiple of 32", (long long)K);
+  REQUIRE(inverse_hadamard != 128 || K % 128 == 0, FP4_E_SHAPE,
+          "fp4_dequantize: the two-level 128 rotation needs K %% 128 == 0 (K=%lld)", (long long)K);
   if (M == 0 || K == 0) return ok();
   REQUIRE(codes && scales && y, FP4_E_NULL, "fp4_dequantize: codes, scales and y are required");
   REQUIRE(fmt == FP4_MXFP4 || tensor_scale, FP4_E_NULL, "fp4_dequantize: NVFP4 needs tensor_scale");

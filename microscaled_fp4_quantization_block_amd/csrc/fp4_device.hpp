@@ -445,6 +445,56 @@ __device__ __forceinline__ void group16_two_level_fwht8(float (&v)[8], int g) {
   for (int j = 0; j < 8; ++j) v[j] *= norm;
 }
 
+// Two-level FWHT of a 128-group spread over the four lanes of a DPP quad, lane p holding
+// elements 32 p .. 32 p + 31 (micro-groups 2 p and 2 p + 1): level 1 is H_16 inside each
+// micro-group (in-lane), level 2 is H_8 across the 8 micro-groups, whose index 2 p + h has
+// the in-lane bit h and the two lane bits of p.  The lane-bit butterflies are the signed
+// form above, so lane p's result carries the sign (-1)^popcount(p), folded into the
+// 1/sqrt(128) normalisation.  Same stage order as two_level_fwht128 on the whole group.
+// All four lanes of the quad must be active.
+__device__ __forceinline__ void quad_two_level_fwht(float* v, int p) {
+  fwht_inplace<16>(v);                 // level 1, micro-group h = 0
+  fwht_inplace<16>(v + 16);            // level 1, micro-group h = 1
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {       // level 2, in-lane bit (h)
+    float a = v[j], b = v[16 + j];
+    v[j] = a + b;
+    v[16 + j] = a - b;
+  }
+  const float c1 = (p & 1) ? -1.0f : 1.0f;
+  const float c2 = (p & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lane_butterflies8_signed<1>(v + 8 * q, c1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lane_butterflies8_signed<2>(v + 8 * q, c2);
+  const float norm = (__popc(p) & 1) ? -InvSqrt<128>::v : InvSqrt<128>::v;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= norm;
+}
+
+// Rotation of a lane's 32-element chunk before quantization: none (H = 0), H_16 / H_32 on
+// whole blocks in-lane, or the two-level 128 transform across the chunk's quad
+// (chunk index % 4 = position in its 128-group; the quad's four lanes must be active).
+template <int H>
+__device__ __forceinline__ void chunk_rotate(float* v, int64_t chunk) {
+  if constexpr (H == 128)
+    quad_two_level_fwht(v, (int)(chunk & 3));
+  else
+    block_hadamard<32, H>(v);
+}
+
+// Inverse rotation of 8 contiguous dequantized values per lane (the transforms are
+// their own inverses): H_16 / H_32 across 2 / 4 lanes of a quad (p = lane % 4), or the
+// two-level 128 transform across 16 lanes (g = lane % 16).  Every lane of the span takes
+// part.
+template <int H>
+__device__ __forceinline__ void unit_rotate8(float (&v)[8], int lane) {
+  if constexpr (H == 128)
+    group16_two_level_fwht8(v, lane & 15);
+  else
+    quad_hadamard8<H>(v, lane & 3);
+}
+
 // --------------------------------------------------------------------------- reductions
 
 template <int N>

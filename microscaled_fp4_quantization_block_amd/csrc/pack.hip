@@ -27,27 +27,6 @@ __device__ __forceinline__ float quad_max(float m) {
   return fmaxf(m, quad_partner<CTRL>(m));
 }
 
-// Two-level FWHT of a 128-group spread over a quad (see file comment), normalised.
-__device__ __forceinline__ void quad_two_level_fwht(float* v, int p) {
-  fwht_inplace<16>(v);                 // level 1, micro-group h = 0
-  fwht_inplace<16>(v + 16);            // level 1, micro-group h = 1
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {       // level 2, in-lane bit (h)
-    float a = v[j], b = v[16 + j];
-    v[j] = a + b;
-    v[16 + j] = a - b;
-  }
-  const float c1 = (p & 1) ? -1.0f : 1.0f;
-  const float c2 = (p & 2) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) lane_butterflies8_signed<1>(v + 8 * q, c1);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) lane_butterflies8_signed<2>(v + 8 * q, c2);
-  const float norm = (__popc(p) & 1) ? -InvSqrt<128>::v : InvSqrt<128>::v;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] *= norm;
-}
-
 __global__ void __launch_bounds__(kThreads)
 k_pack(const uint16_t* x, int64_t nchunks, uint8_t* codes, uint8_t* micro, float* group, float* dbg) {
   int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;

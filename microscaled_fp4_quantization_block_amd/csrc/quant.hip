@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(kAmaxThreads) k_amax(const void* x, int64_t nc
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
     float v[32];
     load_chunk<DT>(x, c, v);
-    block_hadamard<32, H>(v);
+    chunk_rotate<H>(v, c);
     m = fmaxf(m, absmax<32>(v));
   }
   m = wave_max(m);
@@ -63,7 +63,7 @@ k_quant_mx(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales, floa
   if (c >= nchunks) return;
   float v[32];
   load_chunk<DT>(x, c, v);
-  block_hadamard<32, H>(v);
+  chunk_rotate<H>(v, c);
   if (dbg) store_f32<32>(dbg + c * 32, v);
   uint32_t e = e8m0_from_amax(absmax<32>(v));
   reinterpret_cast<uint4*>(codes)[c] = e2m1_encode32(v, e8m0_value(e));
@@ -82,7 +82,7 @@ k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
   const float s_t = *tensor_scale;
   float v[32];
   load_chunk<DT>(x, c, v);
-  block_hadamard<32, H>(v);
+  chunk_rotate<H>(v, c);
   if (dbg) store_f32<32>(dbg + c * 32, v);
   uint2 w[2];
   uint32_t sb[2];
@@ -119,7 +119,6 @@ template <int FMT, int H, int OUT>
 __global__ void __launch_bounds__(kThreads)
 k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t n8, void* y) {
   const int64_t base = (int64_t)blockIdx.x * (kDeqUnits * blockDim.x) + threadIdx.x;
-  const int p = threadIdx.x & 3;
   uint32_t cw[kDeqUnits], sc[kDeqUnits];
 #pragma unroll
   for (int u = 0; u < kDeqUnits; ++u) {
@@ -141,7 +140,7 @@ k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = (v[j] * sb) * s_t;     // V s_b exact
     }
-    quad_hadamard8<H>(v, p);                                    // every lane takes part
+    unit_rotate8<H>(v, threadIdx.x);                            // every lane takes part
     if (i < n8) {
       if constexpr (OUT == fp4impl::DT_F32)
         store_f32<8>(reinterpret_cast<float*>(y) + i * 8, v);
@@ -205,10 +204,12 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t M, int64_t K, int f
   if (dtype == DT_BF16) {
     if (hadamard == 0) return quantize_t<DT_BF16, 0>(x, n, fmt, codes, scales, ts, compute, dbg, st);
     if (hadamard == 16) return quantize_t<DT_BF16, 16>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+    if (hadamard == 128) return quantize_t<DT_BF16, 128>(x, n, fmt, codes, scales, ts, compute, dbg, st);
     return quantize_t<DT_BF16, 32>(x, n, fmt, codes, scales, ts, compute, dbg, st);
   }
   if (hadamard == 0) return quantize_t<DT_F32, 0>(x, n, fmt, codes, scales, ts, compute, dbg, st);
   if (hadamard == 16) return quantize_t<DT_F32, 16>(x, n, fmt, codes, scales, ts, compute, dbg, st);
+  if (hadamard == 128) return quantize_t<DT_F32, 128>(x, n, fmt, codes, scales, ts, compute, dbg, st);
   return quantize_t<DT_F32, 32>(x, n, fmt, codes, scales, ts, compute, dbg, st);
 }
 
@@ -218,10 +219,12 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
   if (fmt == FMT_MX) {
     if (hadamard == 0) return dequant_t<FMT_MX, 0>(codes, scales, ts, n, y, dt, st);
     if (hadamard == 16) return dequant_t<FMT_MX, 16>(codes, scales, ts, n, y, dt, st);
+    if (hadamard == 128) return dequant_t<FMT_MX, 128>(codes, scales, ts, n, y, dt, st);
     return dequant_t<FMT_MX, 32>(codes, scales, ts, n, y, dt, st);
   }
   if (hadamard == 0) return dequant_t<FMT_NV, 0>(codes, scales, ts, n, y, dt, st);
   if (hadamard == 16) return dequant_t<FMT_NV, 16>(codes, scales, ts, n, y, dt, st);
+  if (hadamard == 128) return dequant_t<FMT_NV, 128>(codes, scales, ts, n, y, dt, st);
   return dequant_t<FMT_NV, 32>(codes, scales, ts, n, y, dt, st);
 }
 

@@ -22,7 +22,8 @@ BLOCK = 32
 
 
 def quantize(x, hadamard=0, block_scales=None):
-    """MXFP4 of a 2-D tensor [M, K] after an optional block Hadamard rotation (0/16/32).
+    """MXFP4 of a 2-D tensor [M, K] after an optional block Hadamard rotation (0/16/32, or
+    128 for the two-level 16 x 8 transform).
 
     Returns `packed` [M, K/2] u8, `codes` [M, K], `scales` [M, K/32] u8 (E8M0 codes),
     the rotated values `y`, the block maxima `amax` and the element arguments

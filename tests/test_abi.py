@@ -70,6 +70,8 @@ def _status(fn, *args):
     ((FAKE, 1, 4, 33, 1, 0, FAKE, FAKE, None, 0, None, None), 2),       # K not a multiple of 32
     ((FAKE, 1, -1, 32, 1, 0, FAKE, FAKE, None, 0, None, None), 2),      # negative M
     ((FAKE, 1, 4, 32, 1, 8, FAKE, FAKE, None, 0, None, None), 4),       # unsupported rotation
+    ((FAKE, 1, 4, 256, 1, 64, FAKE, FAKE, None, 0, None, None), 4),     # unsupported rotation
+    ((FAKE, 1, 4, 96, 1, 128, FAKE, FAKE, None, 0, None, None), 2),     # two-level 128 with K % 128 != 0
     ((FAKE, 1, 4, 32, 2, 0, FAKE, FAKE, None, 0, None, None), 4),       # unknown format
     ((FAKE, 7, 4, 32, 1, 0, FAKE, FAKE, None, 0, None, None), 4),       # unknown dtype
     ((FAKE, 1, 4, 32, 0, 0, FAKE, FAKE, None, 0, None, None), 1),       # NVFP4 without tensor scale
@@ -88,6 +90,7 @@ def test_other_entry_points_validation():
     assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 48, 1, 0, FAKE, 0, None)[0] == 2
     assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 64, 0, 0, FAKE, 0, None)[0] == 1
     assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 64, 1, 64, FAKE, 0, None)[0] == 4
+    assert _status("fp4_dequantize", FAKE, FAKE, None, 4, 96, 1, 128, FAKE, 0, None)[0] == 2
     args = [FAKE, 4, 64, None, ctypes.c_float(1e-6), FAKE, 16, FAKE, FAKE, FAKE, 0, None, None]
     bad = list(args); bad[6] = 24                                      # S not a multiple of 16
     assert _status("fp4_residual_quantize", *bad)[0] == 2

@@ -131,7 +131,8 @@ def _check_mx_rotated(x_cpu, h, rows=None):
     g_codes = F.unpack_nibbles(_np(codes)[rows])
     g_scales = _np(scales)[rows]
     ref = mxfp4.quantize(xv, hadamard=h)
-    P.assert_values_close(_np(dbg)[rows], ref["y"], 32, what="rotated values")
+    span = max(32, h)                       # the norm of the tolerance: the rotation's block
+    P.assert_values_close(_np(dbg)[rows], ref["y"], span, what="rotated values")
     P.check_e8m0_scales(g_scales, ref["scales"], ref["amax"])
     cond = mxfp4.quantize(xv, hadamard=h, block_scales=g_scales)
     n = P.check_e2m1_codes(g_codes, cond["codes"], cond["elem_arg"], cond["y"], 32)
@@ -140,15 +141,15 @@ def _check_mx_rotated(x_cpu, h, rows=None):
     assert np.array_equal(_np(y_f32)[rows].astype(np.float64), want)
     # ... and one bf16 rounding of the fp32 inverse rotation with it
     want_h = mxfp4.dequantize(_np(codes)[rows], g_scales, inverse_hadamard=h)
-    P.assert_bf16_close(_vals(y_bf16.cpu())[rows], want_h, 32)
+    P.assert_bf16_close(_vals(y_bf16.cpu())[rows], want_h, span)
     return n
 
 
-@pytest.mark.parametrize("h", [16, 32])
+@pytest.mark.parametrize("h", [16, 32, 128])
 def test_mxfp4_rotated_small(h):
     _log(f"mxfp4 H{h} small")
     rng = np.random.default_rng(h)
-    x = rng.standard_normal((37, 224))
+    x = rng.standard_normal((37, 384 if h == 128 else 224))
     x[:, 3] *= 50
     x[5] = 1.0                                   # constant rows: exact zeros after H
     _check_mx_rotated(W.to_bf16(x), h)
@@ -162,7 +163,31 @@ def test_mxfp4_h32_config_full_size():
     _log(f"  boundary-tolerated code differences: {n}")
 
 
-@pytest.mark.parametrize("h", [16, 32])
+def test_two_level_128_on_the_student_t_workload():
+    """The two-level 128 rotation through fp4_quantize on the dual-scale workload's input
+    (bf16 8192 x 8192 Student-t(4), first 1024 rows), MXFP4 and NVFP4 (dynamic tensor scale
+    over all 8192 rows), then the inverse-128 dequantization of the GPU's own codes."""
+    _log("H128 mxfp4 + nvfp4 on Student-t(4) 8192x8192")
+    x = W.student_t_input()
+    _check_mx_rotated(x[:1024].contiguous(), 128)
+    xg = x.to(DEV)
+    dbg = torch.empty(x.shape, dtype=torch.float32, device=DEV)
+    codes, scales, ts = fp4.fp4_quantize(xg, "nvfp4", 128, dbg_rotated=dbg)
+    gst = _np(ts)[0]
+    assert gst == np.float32(np.max(np.abs(_np(dbg)))) / np.float32(2688.0)
+    rows = W.seeded_rows(8192, 256, 128)
+    xv = _vals(x)[rows]
+    ref = nvfp4.quantize(xv, hadamard=128, tensor_scale_value=gst)
+    P.assert_values_close(_np(dbg)[rows], ref["y"], 128, what="rotated values")
+    P.check_e4m3_scales(_np(scales)[rows], ref["scales"], ref["scale_arg"])
+    c2 = nvfp4.quantize(xv, hadamard=128, tensor_scale_value=gst, block_scales=_np(scales)[rows])
+    P.check_e2m1_codes(F.unpack_nibbles(_np(codes)[rows]), c2["codes"], c2["elem_arg"], c2["y"], 16)
+    y = fp4.fp4_dequantize(codes, scales, ts, "nvfp4", 128, torch.bfloat16)
+    want = nvfp4.dequantize(_np(codes)[rows], _np(scales)[rows], gst, inverse_hadamard=128)
+    P.assert_bf16_close(_vals(y.cpu())[rows], want, 128)
+
+
+@pytest.mark.parametrize("h", [16, 32, 128])
 def test_nvfp4_rotated(h):
     _log(f"nvfp4 H{h}")
     rng = np.random.default_rng(100 + h)
@@ -177,6 +202,7 @@ def test_nvfp4_rotated(h):
     P.assert_values_close(_np(dbg), ref["y"], h, what="rotated values")
     gst = _np(ts)[0]
     P.assert_rel(gst, ref["tensor_scale"], what="tensor scale")
+    assert gst == np.float32(np.max(np.abs(_np(dbg)))) / np.float32(2688.0)   # of the kernel's own values
     c1 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst)
     P.check_e4m3_scales(_np(scales), c1["scales"], c1["scale_arg"])
     c2 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst, block_scales=_np(scales))
@@ -187,15 +213,15 @@ def test_nvfp4_rotated(h):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-@pytest.mark.parametrize("h", [0, 16, 32])
+@pytest.mark.parametrize("h", [0, 16, 32, 128])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_dequantize_every_variant(fmt, h, out):
     """Dequantization of the GPU's own codes against the oracle's dequantization of the same
     codes, for every format, rotation and output type, on a shape whose unit count leaves a
-    partial last workgroup (37 x 224)."""
+    partial last workgroup (37 x 224, or 37 x 384 for the 128 rotation)."""
     _log(f"dequant {fmt} H{h} {out}")
     rng = np.random.default_rng(7 + h)
-    x = rng.standard_normal((37, 224))
+    x = rng.standard_normal((37, 384 if h == 128 else 224))
     x[:, 9] *= 30
     xg = W.to_bf16(x).to(DEV)
     codes, scales, ts = fp4.fp4_quantize(xg, fmt, 0)
@@ -242,13 +268,14 @@ def test_dequantize_every_scale_byte(fmt):
     assert np.array_equal(got[~nan].view(np.uint32), want32[~nan].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt,h", [("mxfp4", 32), ("mxfp4", 16), ("nvfp4", 16), ("nvfp4", 32)])
+@pytest.mark.parametrize("fmt,h", [("mxfp4", 32), ("mxfp4", 16), ("nvfp4", 16), ("nvfp4", 32), ("mxfp4", 128),
+                                   ("nvfp4", 128)])
 def test_rotated_fp32_input(fmt, h):
     """fp32 input (not only bf16) through the rotated quantizers: rotated values, scales
     and codes against the oracle under the boundary rule."""
     _log(f"{fmt} H{h} fp32 input")
     rng = np.random.default_rng(200 + h)
-    x = rng.standard_normal((29, 192)).astype(np.float32)
+    x = rng.standard_normal((29, 384 if h == 128 else 192)).astype(np.float32)
     x[:, 11] *= 25
     xg = torch.from_numpy(x).to(DEV)
     xv = x.astype(np.float64)
@@ -257,7 +284,7 @@ def test_rotated_fp32_input(fmt, h):
     gc, gs = F.unpack_nibbles(_np(codes)), _np(scales)
     if fmt == "mxfp4":
         ref = mxfp4.quantize(xv, hadamard=h)
-        P.assert_values_close(_np(dbg), ref["y"], 32, what="rotated values")
+        P.assert_values_close(_np(dbg), ref["y"], max(32, h), what="rotated values")
         P.check_e8m0_scales(gs, ref["scales"], ref["amax"])
         c = mxfp4.quantize(xv, hadamard=h, block_scales=gs)
         P.check_e2m1_codes(gc, c["codes"], c["elem_arg"], c["y"], 32)

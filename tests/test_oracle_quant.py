@@ -169,6 +169,28 @@ def test_mxfp4_rotation_applied_before_quantization():
     assert abs(err_back - err_rot) < 1e-9 * err_rot
 
 
+def test_two_level_128_rotation_before_nvfp4_and_mxfp4():
+    """hadamard=128 quantizes scipy's H_128 of every 128-group (the two-level 16 x 8
+    transform equals it), and the inverse rotation on dequantization maps back."""
+    import scipy.linalg
+    rng = np.random.default_rng(24)
+    x = rng.standard_t(4, (3, 384))
+    h = scipy.linalg.hadamard(128) / np.sqrt(128.0)
+    xr = (x.reshape(3, 3, 128) @ h.T).reshape(3, 384)
+    a, b = nvfp4.quantize(x, hadamard=128), nvfp4.quantize(xr)
+    assert np.allclose(a["y"], xr, rtol=0, atol=1e-13)
+    assert np.array_equal(a["scales"], b["scales"])
+    assert np.mean(a["codes"] == b["codes"]) > 0.999          # a few ulp of y may cross a midpoint
+    m = mxfp4.quantize(x, hadamard=128)
+    back = mxfp4.dequantize(m["packed"], m["scales"], inverse_hadamard=128)
+    err_back = np.linalg.norm(back - x)
+    err_rot = np.linalg.norm(mxfp4.dequantize(m["packed"], m["scales"]) - m["y"])
+    assert abs(err_back - err_rot) < 1e-9 * err_rot
+    d = nvfp4.dequantize(a["packed"], a["scales"], a["tensor_scale"], inverse_hadamard=128)
+    assert np.allclose(d, (nvfp4.dequantize(a["packed"], a["scales"], a["tensor_scale"]).reshape(3, 3, 128)
+                           @ h.T).reshape(3, 384), rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- dual scale
 
 def test_dualscale_quantization_against_exact_bruteforce():
