@@ -52,7 +52,6 @@ constexpr int kMaxGroups = 8;       // load groups of two waves, at most 16 wave
 constexpr int kStatsGroups = 256;
 
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
-__global__ void k_finalize_tensor_scale(float* p) { *p = *p / 2688.0f; }
 
 // Make this wave's LDS writes visible to its own later LDS reads (and the reverse).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -128,16 +127,18 @@ __device__ __forceinline__ float norm_value(uint16_t xb, float inv_rms, float g)
   return kGamma ? y * g : y;
 }
 
-// Maximum of m over the workgroup, then one atomic max into *dst.  Every thread of the
-// workgroup calls it (it holds a barrier).
-__device__ __forceinline__ void workgroup_atomic_max(float m, float* dst) {
+// Maximum m of max|z| over the workgroup, then one atomic max of fl32(m / 2688) into the
+// tensor scale *ts (which starts at 0).  Correctly rounded division by a positive constant
+// is monotone, so the largest rounded quotient is fl32(max|z| / 2688) of the whole tensor.
+// Every thread of the workgroup calls it (it holds a barrier).
+__device__ __forceinline__ void workgroup_tensor_scale(float m, float* ts) {
   __shared__ float wmax[kMaxWaves];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, wmax[w]);
-    if (m > 0.0f) atomic_max_nonneg(dst, m);
+    if (m > 0.0f) atomic_max_nonneg(ts, m / 2688.0f);
   }
 }
 
@@ -171,7 +172,7 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
     }
     wave_lds_sync();
   }
-  workgroup_atomic_max(tmax, tensor_scale);
+  workgroup_tensor_scale(tmax, tensor_scale);
 }
 
 // Statistics pass for rows of at most 64 kUnroll units: rows stay in registers (no LDS
@@ -234,7 +235,7 @@ k_arc_stats_rows(const uint16_t* __restrict__ x, int64_t M, int K, const float* 
     tmax = fmaxf(tmax, row_absmax<kGamma>(a, units, lane, K, eps, gamma));
     tmax = fmaxf(tmax, row_absmax<kGamma>(b, units, lane, K, eps, gamma));
   }
-  workgroup_atomic_max(tmax, tensor_scale);
+  workgroup_tensor_scale(tmax, tensor_scale);
 }
 
 // Encode one 16-channel block: primary NVFP4 codes and scale, and for blocks inside the
@@ -579,7 +580,6 @@ hipError_t launch_arc(const uint16_t* x, int64_t M, int64_t K, const float* gamm
       k_arc_stats<kGamma><<<a.grid < kStatsGroups ? a.grid : kStatsGroups, 64 * a.W, a.lds_stats, st>>>(
           x, M, (int)K, gamma, eps, ts);
     }
-    k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
   if (M)
     k_arcquant<FMT, kGamma><<<a.grid_q, 64 * a.Wq, a.lds_quant, st>>>(x, M, (int)K, gamma, eps, perm, (int)S,

@@ -109,13 +109,14 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
 }
 
-// The resource `r` advanced by `col` bytes: base + col, and col fewer bytes in range.  The
+// The resource `r` advanced by `col` bytes: base + col, and col fewer bytes in range (none
+// if col exceeds them; the count saturates at 0 rather than wrapping round to 4 GiB).  The
 // raw-buffer range check covers the VGPR offset but not an SGPR one, so a K-column offset
 // goes into the base instead: every byte fetched then lies inside the operand or reads as
-// zero.  Wave-uniform scalar arithmetic; col < r's size (col < K / 2 <= the row bytes).
+// zero.  Wave-uniform scalar arithmetic.
 __device__ __forceinline__ u32x4 advance_rsrc(const u32x4& r, uint32_t col) {
   const uint64_t a = ((uint64_t)(r[1] & 0xffffu) << 32 | r[0]) + col;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, r[2] - col, r[3]};
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, r[2] > col ? r[2] - col : 0u, r[3]};
 }
 
 // 16 bytes per lane from buffer offset voff + soff straight into LDS at lds + 16 lane (one
@@ -168,6 +169,9 @@ __device__ __forceinline__ int rotated(const LD& L, int p) {
 // first bytes, or zero past the last row; their scales are zeroed before use.
 template <class LD>
 __device__ __forceinline__ void issue_codes(const LD& L, int p, bool valid, uint8_t* dst) {
+  // Past the end of K, rotated() wraps to a buffer index whose column may exceed a short
+  // operand's bytes; advance_rsrc then leaves no bytes in range, and in any case at most
+  // the operand's (< 2^31), so the kOOB offset of such an issue stays out of range.
   const uint32_t col = (uint32_t)rotated(L, p) * ROWB;
   const u32x4 ra = LD::kTail ? advance_rsrc(L.rA, col) : L.rA;
   const u32x4 rb = LD::kTail ? advance_rsrc(L.rB, col) : L.rB;

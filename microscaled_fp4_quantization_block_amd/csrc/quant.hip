@@ -5,7 +5,8 @@
 // Hadamard blocks (16 or 32), one MXFP4 block or two NVFP4 blocks, so rotation, block
 // maxima, scale choice and encoding all stay in the lane's registers; the only
 // cross-lane step is the per-tensor maximum of NVFP4 (a grid-stride pass before the
-// quantization launch, reduced over each workgroup before its one atomic).
+// quantization launch, reduced over each workgroup before its one atomic), and for the
+// two-level 128 rotation the DPP butterflies across a quad of chunks.
 //
 // Sources: MR-GPTQ abstract (hyper.ai, Résumé) for block Hadamard before MXFP4 / NVFP4
 // quantization and online activation rotation; ARCQuant summary (gist.science, Énoncé du
@@ -30,15 +31,15 @@ __device__ __forceinline__ void load_chunk(const void* x, int64_t chunk, float* 
 
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 
-// s_t = fl32(amax / 2688), in place (correctly rounded fp32 division).
-__global__ void k_finalize_tensor_scale(float* p) { *p = *p / kTensorDivisor; }
-
-// Per-tensor maximum of |H x| (running atomic max into *amax, which starts at 0).  A
-// grid-stride walk over the chunks, reduced over the workgroup before its one atomic:
-// atomics on a single address serialise, so the grid is capped at kAmaxGroups.
+// Tensor scale s_t = fl32(max|H x| / 2688) by a running atomic max into *ts (which starts
+// at 0).  A grid-stride walk over the chunks, reduced over the workgroup before its one
+// atomic: atomics on a single address serialise, so the grid is capped at kAmaxGroups.
+// Each workgroup contributes fl32(m / 2688) of its own maximum m: correctly rounded
+// division by a positive constant is monotone, so the maximum of the rounded quotients is
+// the rounded quotient of the maximum, and no finishing step is needed.
 constexpr int kAmaxThreads = 1024, kAmaxGroups = 256;
 template <int DT, int H>
-__global__ void __launch_bounds__(kAmaxThreads) k_amax(const void* x, int64_t nchunks, float* amax) {
+__global__ void __launch_bounds__(kAmaxThreads) k_amax(const void* x, int64_t nchunks, float* ts) {
   __shared__ float wm[kAmaxThreads / 64];
   float m = 0.0f;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
@@ -52,7 +53,7 @@ __global__ void __launch_bounds__(kAmaxThreads) k_amax(const void* x, int64_t nc
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, wm[w]);
-    if (m > 0.0f) atomic_max_nonneg(amax, m);
+    if (m > 0.0f) atomic_max_nonneg(ts, m / kTensorDivisor);
   }
 }
 
@@ -173,7 +174,6 @@ hipError_t quantize_t(const void* x, int64_t nchunks, int fmt, uint8_t* codes, u
       const int64_t wg = (nchunks + t - 1) / t;
       k_amax<DT, H><<<dim3((unsigned)(wg < kAmaxGroups ? wg : kAmaxGroups)), dim3((unsigned)t), 0, st>>>(x, nchunks, ts);
     }
-    k_finalize_tensor_scale<<<1, 1, 0, st>>>(ts);
   }
   if (nchunks) k_quant_nv<DT, H><<<g, b, 0, st>>>(x, nchunks, codes, scales, ts, dbg);
   return hipGetLastError();

@@ -13,7 +13,10 @@ against the operand's size:
 * otherwise (a half last buffer, or a half last scale group): the column offset moves into
   the resource base and out of num_records, so the check covers it.
 
-The same model with the first scheme on a ragged K shows the overrun the second prevents.
+Every issued load is modelled, including those past the end of K, whose offset is an
+out-of-range sentinel: the resource count saturates at zero when the column exceeds it, so
+the sentinel stays out of range.  The same model with the first scheme on a ragged K, or
+with a count that wraps round, shows the overruns the kernel prevents.
 """
 import numpy as np
 import pytest
@@ -49,17 +52,36 @@ def _lane_offsets(rowbytes, rowscales):
     return codes, scales
 
 
-def _fetched_max(M, N, K, tail):
+KOOB = 1 << 31          # the kernel's offset for an issue past the end of K
+
+
+def _issues(np_):
+    """(code buffer index or scale group, valid) in the kernel's issue order: the prologue
+    (scale group 0, buffers 0 and 1, the latter out of range when np == 1), then at step p
+    buffer p + 2 and, on even steps, scale group (p + 2) / 2, valid only below np."""
+    codes = [(0, True), (1, np_ > 1)] + [(p + 2, p + 2 < np_) for p in range(np_)]
+    scales = [(0, True)] + [((p + 2) >> 1, p + 2 < np_) for p in range(0, np_, 2)]
+    return codes, scales
+
+
+def _fetched_max(M, N, K, tail, wrap=False):
     """Largest byte offset + 1 fetched from each operand (A codes, B codes, A scales,
-    B scales) over every tile and load, or -1 if none."""
+    B scales) over every tile and issued load, or -1 if none.  `wrap` models a resource
+    count that wraps round instead of saturating when the column exceeds it."""
     rowbytes, rowscales = K // 2, K // 32
     np_ = (K + BKP - 1) // BKP
     tiles_m, tiles_n = (M + BM - 1) // BM, (N + BN - 1) // BN
     codes_off, scale_off = _lane_offsets(rowbytes, rowscales)
+    code_issues, scale_issues = _issues(np_)
     top = {"a": -1, "b": -1, "sa": -1, "sb": -1}
 
-    def admit(key, base, nrec, voff, soff):
-        voff = np.asarray(voff, dtype=np.int64)
+    def admit(key, base, nrec, col, voff, valid):
+        if tail:
+            base, soff = base + col, 0
+            nrec = (nrec - col) % (1 << 32) if wrap else max(nrec - col, 0)
+        else:
+            soff = col
+        voff = np.asarray(voff, dtype=np.int64) if valid else np.full(64, KOOB, dtype=np.int64)
         for d in range(4):                      # the four dwords of a 16-byte load
             ok = voff + 4 * d + 4 <= nrec
             if ok.any():
@@ -70,29 +92,24 @@ def _fetched_max(M, N, K, tail):
             m0, n0 = tm * BM, tn * BN
             rows_a, rows_b = min(BM, M - m0), min(BN, N - n0)
             rot = (2 * tm) % np_ if K % (2 * BKP) == 0 else 0
-            for p in range(np_):
-                col = ((p + rot) % np_) * ROWB
+
+            def rotated(q):
+                q += rot
+                return q - np_ if q >= np_ else q
+
+            for q, valid in code_issues:
+                col = rotated(q) * ROWB
                 for key, r0, rows in (("a", m0, rows_a), ("b", n0, rows_b)):
-                    base, nrec = r0 * rowbytes, rows * rowbytes
-                    if tail:
-                        base, nrec, soff = base + col, nrec - col, 0
-                    else:
-                        soff = col
                     for wave in range(NW):
-                        for q in range(QW):
-                            admit(key, base, nrec, codes_off[wave][q], soff)
-            for h in range((np_ + 1) // 2):
-                col = (((2 * h + rot) % np_) >> 1) * KSCALE_ROW
+                        for i in range(QW):
+                            admit(key, r0 * rowbytes, rows * rowbytes, col, codes_off[wave][i], valid)
+            for h, valid in scale_issues:
+                col = (rotated(2 * h) >> 1) * KSCALE_ROW
                 for wave in range(NW):
-                    for q in range(SW):
-                        t = SW * wave + q
+                    for i in range(SW):
+                        t = SW * wave + i
                         key, r0, rows = ("sb", n0, rows_b) if t >> 2 else ("sa", m0, rows_a)
-                        base, nrec = r0 * rowscales, rows * rowscales
-                        if tail:
-                            base, nrec, soff = base + col, nrec - col, 0
-                        else:
-                            soff = col
-                        admit(key, base, nrec, scale_off[wave][q], soff)
+                        admit(key, r0 * rowscales, rows * rowscales, col, scale_off[wave][i], valid)
     return top
 
 
@@ -113,6 +130,17 @@ def test_every_fetched_byte_is_inside_its_operand(M, N, K):
     for key in top:
         assert top[key] <= size[key], (key, top[key], size[key])
     assert top["a"] == size["a"] and top["b"] == size["b"]   # and the last row is read whole
+
+
+def test_a_wrapping_resource_count_would_admit_the_sentinel():
+    """M = N = 1, K = 128: past the end, rotated() wraps step 0's refill (q = 2) to buffer
+    1, whose column (128) exceeds the operand's 64 bytes.  A count that wraps round to
+    4 GiB admits the out-of-range offset and fetches 2 GiB past the operand; the
+    saturating count admits nothing beyond it."""
+    top = _fetched_max(1, 1, 128, tail=True, wrap=True)
+    assert top["a"] > (1 << 31)
+    top = _fetched_max(1, 1, 128, tail=True)
+    assert top["a"] == 64 and top["b"] == 64
 
 
 def test_sgpr_column_offset_would_overrun_on_a_ragged_k():
