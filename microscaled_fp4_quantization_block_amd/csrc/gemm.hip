@@ -30,8 +30,7 @@
 //   the sixteen lanes that share an LDS pass (one chunk of sixteen consecutive rows)
 //   touch sixteen distinct 16-byte bank groups.
 // - Buffer resources are built per tile: rows past M or N fall outside the resource and
-//   read as zero (never fault), and only feed outputs that are not stored.  Every load's
-//   full offset is in its VGPR, which the range check covers.
+//   read as zero (never fault), and only feed outputs that are not stored.
 // - Tiles are assigned XCD-aware: consecutive workgroup ids land on different XCDs, so the
 //   id is remapped to give every XCD a contiguous band of tiles, walked in groups of 8
 //   tile-rows, keeping each XCD's L2 working set to a few A and B panels.
@@ -109,21 +108,11 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
 }
 
-// The resource `r` advanced by `col` bytes: base + col, and col fewer bytes in range (none
-// if col exceeds them; the count saturates at 0 rather than wrapping round to 4 GiB).  The
-// raw-buffer range check covers the VGPR offset but not an SGPR one, so a K-column offset
-// goes into the base instead: every byte fetched then lies inside the operand or reads as
-// zero.  Wave-uniform scalar arithmetic.
-__device__ __forceinline__ u32x4 advance_rsrc(const u32x4& r, uint32_t col) {
-  const uint64_t a = ((uint64_t)(r[1] & 0xffffu) << 32 | r[0]) + col;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, r[2] > col ? r[2] - col : 0u, r[3]};
-}
-
-// 16 bytes per lane from buffer offset voff + soff straight into LDS at lds + 16 lane (one
-// wait state between the M0 write and the load that reads it).
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at lds + 16 lane
+// (one wait state between the M0 write and the load that reads it).
 // Written as one asm statement (M0 set and the load issued together; it has no register
 // results) so the compiler neither sees nor waits on the LDS write: every wait for these
-// loads is an explicit vmcnt before a workgroup barrier.
+// loads is the explicit vmcnt(0) before a workgroup barrier.
 __device__ __forceinline__ void dma16(const u32x4& rsrc, const uint8_t* lds, uint32_t voff, uint32_t soff) {
   const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -135,15 +124,10 @@ __device__ __forceinline__ void dma16(const u32x4& rsrc, const uint8_t* lds, uin
 // Per-thread loader state.  Per buffer and operand, 32 code instructions (8 rows x 128
 // bytes = 1 KiB each) are split over the waves, QW = 32 / NW each; per scale group and
 // operand, 4 instructions (64 rows x 16 bytes), SW = 8 / NW per wave over both operands.
-template <int NW, bool TAIL>
+template <int NW>
 struct Loader {
   static constexpr int QW = 32 / NW;
   static constexpr int SW = 8 / NW;
-  // K % 512 != 0: the last code buffer or scale group runs past the end of a row, so the
-  // K-column offset goes into the resource base (covered by the range check) instead of
-  // the SGPR offset.  With K % 512 == 0 every access stays inside its row: a code buffer
-  // ends at column 128 (p + 1) <= K / 2 and a scale group at 16 (h + 1) <= K / 32.
-  static constexpr bool kTail = TAIL;
   u32x4 rA, rB, rSA, rSB;   // buffer descriptors (wave-uniform, SGPRs)
   uint32_t code_off[2];   // lane offset of instruction 0 (even) / 1 (odd); +8 q rows per q
   uint32_t row_step;      // 8 rows in bytes
@@ -153,8 +137,8 @@ struct Loader {
 };
 
 // Buffer that the tile processes at step p: p + rot, wrapped into [0, np).
-template <class LD>
-__device__ __forceinline__ int rotated(const LD& L, int p) {
+template <int NW>
+__device__ __forceinline__ int rotated(const Loader<NW>& L, int p) {
   const int q = p + L.rot;
   return q >= L.np ? q - L.np : q;
 }
@@ -162,26 +146,17 @@ __device__ __forceinline__ int rotated(const LD& L, int p) {
 // Issue buffer p (K elements 256 p ..) of both operands into `dst`.  Code instruction g
 // fills bytes [g KiB, +1 KiB): lane l lands at byte 16 l = row 8 g + l / 8, slot l % 8,
 // holding global chunk (l % 8) ^ swz(row) (which depends on g only through g % 2).
-// `valid` false (a buffer past the end of K) issues the instructions with every offset
-// out of range: no memory traffic, zeros into a slot that is dead by then, and straight
-// control flow (a branch here splits the pipelined loop and costs registers).  In a
-// ragged last buffer (K % 256 == 128) the chunks past a row's end read the next row's
-// first bytes, or zero past the last row; their scales are zeroed before use.
-template <class LD>
-__device__ __forceinline__ void issue_codes(const LD& L, int p, bool valid, uint8_t* dst) {
-  // Past the end of K, rotated() wraps to a buffer index whose column may exceed a short
-  // operand's bytes; advance_rsrc then leaves no bytes in range, and in any case at most
-  // the operand's (< 2^31), so the kOOB offset of such an issue stays out of range.
-  const uint32_t col = (uint32_t)rotated(L, p) * ROWB;
-  const u32x4 ra = LD::kTail ? advance_rsrc(L.rA, col) : L.rA;
-  const u32x4 rb = LD::kTail ? advance_rsrc(L.rB, col) : L.rB;
-  const uint32_t soff = LD::kTail ? 0u : col;
+// `valid` false issues the instructions with every offset out of range (no memory
+// traffic), keeping the control flow straight.
+template <int NW>
+__device__ __forceinline__ void issue_codes(const Loader<NW>& L, int p, bool valid, uint8_t* dst) {
+  const int soff = rotated(L, p) * ROWB;
 #pragma unroll
-  for (int q = 0; q < LD::QW; ++q) {
-    uint8_t* blk = dst + (LD::QW * L.wave + q) * 1024;
+  for (int q = 0; q < Loader<NW>::QW; ++q) {
+    uint8_t* blk = dst + (Loader<NW>::QW * L.wave + q) * 1024;
     const uint32_t off = valid ? L.code_off[q & 1] + (uint32_t)(q & ~1) * L.row_step : kOOB;
-    dma16(ra, blk, off, soff);
-    dma16(rb, blk + kCodeBytes, off, soff);
+    dma16(L.rA, blk, off, soff);
+    dma16(L.rB, blk + kCodeBytes, off, soff);
   }
 }
 
@@ -189,16 +164,14 @@ __device__ __forceinline__ void issue_codes(const LD& L, int p, bool valid, uint
 // tile's starting buffer) into `dst` ([A rows][16 B] then [B rows][16 B]); instruction t
 // covers rows 64 (t % 4) + l of operand t / 4.  rot is even, so a group never straddles
 // the wrap.
-template <class LD>
-__device__ __forceinline__ void issue_scales(const LD& L, int h, bool valid, uint8_t* dst) {
-  const uint32_t col = (uint32_t)(rotated(L, 2 * h) >> 1) * kScaleRow;
-  const uint32_t soff = LD::kTail ? 0u : col;
+template <int NW>
+__device__ __forceinline__ void issue_scales(const Loader<NW>& L, int h, bool valid, uint8_t* dst) {
+  const int soff = (rotated(L, 2 * h) >> 1) * kScaleRow;
 #pragma unroll
-  for (int q = 0; q < LD::SW; ++q) {
-    const int t = LD::SW * L.wave + q;
+  for (int q = 0; q < Loader<NW>::SW; ++q) {
+    const int t = Loader<NW>::SW * L.wave + q;
     uint8_t* blk = dst + (t >> 2) * kScaleBytes + (t & 3) * 1024;
-    const u32x4& r = (t >> 2) ? L.rSB : L.rSA;
-    dma16(LD::kTail ? advance_rsrc(r, col) : r, blk, valid ? L.scale_off[q] : kOOB, soff);
+    dma16((t >> 2) ? L.rSB : L.rSA, blk, valid ? L.scale_off[q] : kOOB, soff);
   }
 }
 
@@ -287,10 +260,10 @@ __device__ __forceinline__ void interleave_reads() {
 // buffer p + 2.  Past the end the loads go out of range: they move no data but still
 // write zeros to LDS, into slots that are dead by then (`cur` after its last read, and a
 // scale slot whose group was last read two steps earlier).
-template <int NW, bool kRefillScales, class LD>
+template <int NW, bool kRefillScales>
 __device__ __forceinline__ void run_buffer(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], Frags<NW> (&f)[2],
                                            u32x2 (&sa)[Cfg<NW>::TI], u32x2 (&sb)[Cfg<NW>::TJ],
-                                           const LD& L, int p, int np, bool ragged,
+                                           const Loader<NW>& L, int p, int np, bool ragged,
                                            uint8_t* cur, const uint8_t* next,
                                            uint8_t* sgrp_refill, const uint8_t* sgrp_next,
                                            int wm, int wn, int r32, int khalf) {
@@ -309,8 +282,8 @@ __device__ __forceinline__ void run_buffer(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ]
   read_scales<NW>(sgrp_next, p + 1, ragged && p + 1 == np - 1, wm, wn, r32, na, nb);
   read_codes<NW>(next, 0, wm, wn, r32, khalf, f[0]);
   const int q = p + 2;
-  if constexpr (kRefillScales) issue_scales(L, q >> 1, q < np, sgrp_refill);
-  issue_codes(L, q, q < np, cur);
+  if constexpr (kRefillScales) issue_scales<NW>(L, q >> 1, q < np, sgrp_refill);
+  issue_codes<NW>(L, q, q < np, cur);
   mfma_substep<NW>(acc, f[1], sa, sb, 3, khalf);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -324,20 +297,16 @@ __device__ __forceinline__ void run_buffer(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ]
 // slots arrive as restrict pointers of this one function, so the compiler knows for the
 // whole loop that a DMA into one slot never overlaps reads of another and adds no waits
 // of its own (the loop-carried DMA would otherwise cost a full drain per buffer).
-template <int NW, class LD>
-__device__ __forceinline__ void k_loop(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], const LD& L, int np,
+template <int NW>
+__device__ __forceinline__ void k_loop(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], const Loader<NW>& L, int np,
                                        bool ragged, uint8_t* __restrict__ c0, uint8_t* __restrict__ c1,
                                        uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, int wm, int wn,
                                        int r32, int khalf) {
-  // prologue: scale group 0 and buffers 0 and 1 in flight (buffer 1's loads out of range
-  // when np == 1, but issued all the same).  Loads complete in issue order, so once at
-  // most buffer 1's 2 QW loads are outstanding, scale group 0 and buffer 0 have landed;
-  // buffer 1 is waited for at the first step's barrier.
-  issue_scales(L, 0, true, s0);
-  issue_codes(L, 0, true, c0);
-  issue_codes(L, 1, np > 1, c1);
-  static_assert(2 * LD::QW == 8, "vmcnt below counts buffer 1's loads");
-  __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) expcnt(7) lgkmcnt(0)
+  // prologue: buffers 0 and 1 and scale group 0 in flight
+  issue_scales<NW>(L, 0, true, s0);
+  issue_codes<NW>(L, 0, true, c0);
+  issue_codes<NW>(L, 1, np > 1, c1);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   Frags<NW> f[2];
   u32x2 sa[Cfg<NW>::TI], sb[Cfg<NW>::TJ];
@@ -351,7 +320,7 @@ __device__ __forceinline__ void k_loop(v16f (&acc)[Cfg<NW>::TI][Cfg<NW>::TJ], co
   }
 }
 
-template <int NW, bool TAIL>
+template <int NW>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
@@ -370,7 +339,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
   const int np = (K + BKP - 1) / BKP;              // K % 128 == 0
   const bool ragged = (K % BKP) != 0;              // last buffer holds 128 elements
 
-  Loader<NW, TAIL> L;
+  Loader<NW> L;
   {
     const uint32_t rows_a = (uint32_t)min(BM, M - tile.m0), rows_b = (uint32_t)min(BN, N - tile.n0);
     L.rA = make_rsrc(A + (size_t)tile.m0 * rowbytes, rows_a * rowbytes);
@@ -379,13 +348,13 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
     L.rSB = make_rsrc(SB + (size_t)tile.n0 * rowscales, rows_b * rowscales);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int row = 8 * (Loader<NW, TAIL>::QW * wave + q) + (lane >> 3);
+      const int row = 8 * (Loader<NW>::QW * wave + q) + (lane >> 3);
       L.code_off[q] = (uint32_t)row * rowbytes + 16u * (uint32_t)((lane & 7) ^ swz(row));
     }
     L.row_step = 8u * rowbytes;
 #pragma unroll
-    for (int q = 0; q < Loader<NW, TAIL>::SW; ++q) {
-      const int t = Loader<NW, TAIL>::SW * wave + q;
+    for (int q = 0; q < Loader<NW>::SW; ++q) {
+      const int t = Loader<NW>::SW * wave + q;
       L.scale_off[q] = (uint32_t)(64 * (t & 3) + lane) * rowscales;
     }
     L.wave = wave;
@@ -489,10 +458,7 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
                        int64_t M, int64_t N, int64_t K, void* c, int ctype, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (K % (2 * BKP) == 0)
-    k_gemm<kWaves, false><<<dim3((unsigned)tiles), dim3(64 * kWaves), 0, st>>>(a, sa, b, sb, (int)M, (int)N, (int)K, c, ctype);
-  else
-    k_gemm<kWaves, true><<<dim3((unsigned)tiles), dim3(64 * kWaves), 0, st>>>(a, sa, b, sb, (int)M, (int)N, (int)K, c, ctype);
+  k_gemm<kWaves><<<dim3((unsigned)tiles), dim3(64 * kWaves), 0, st>>>(a, sa, b, sb, (int)M, (int)N, (int)K, c, ctype);
   return hipGetLastError();
 }
 

@@ -1,22 +1,22 @@
-"""Host-side model of the W4A4 GEMM's global -> LDS loads: every byte the hardware may
-fetch lies inside its operand.
+"""Host-side model of the W4A4 GEMM's global -> LDS loads: where the hardware may fetch.
 
-The kernel loads 16 bytes per lane through raw buffer resources.  The range check of a
-raw resource covers the VGPR offset only; an SGPR offset is added to the address after
-it.  The model mirrors the kernel's offset arithmetic (tile rows, the K walk's starting
-buffer, the XOR chunk swizzle, the scale groups), assumes the check admits a dword when
-VGPR offset + 4 (dword end) <= num_records, and checks the admitted dwords' addresses
-against the operand's size:
+The kernel loads 16 bytes per lane through raw buffer resources over each tile's rows.  The
+range check of a raw resource covers the VGPR offset only (row and 16-byte chunk here); the
+SGPR offset (the K column) is added to the address after it.  The model mirrors the
+kernel's offset arithmetic (tile rows, the K walk's starting buffer, the XOR chunk swizzle,
+the scale groups, every issue including those past the end of K with their out-of-range
+sentinel), assumes the check admits a dword when VGPR offset + 4 <= num_records, and
+compares the admitted dwords' addresses with the operand's size.
 
-* K % 512 == 0: the K-column offset rides in the SGPR offset; every code buffer ends by
-  column K / 2 and every scale group by K / 32, so nothing leaves its row.
-* otherwise (a half last buffer, or a half last scale group): the column offset moves into
-  the resource base and out of num_records, so the check covers it.
-
-Every issued load is modelled, including those past the end of K, whose offset is an
-out-of-range sentinel: the resource count saturates at zero when the column exceeds it, so
-the sentinel stays out of range.  The same model with the first scheme on a ragged K, or
-with a count that wraps round, shows the overruns the kernel prevents.
+* K % 512 == 0: every code buffer ends by column K / 2 and every scale group by K / 32, so
+  nothing leaves its row: every fetched byte is inside the operand.
+* Otherwise (a half last buffer, or a half last scale group) the last buffer's chunks past
+  a row's end are admitted and read the next row, and at the operand's last row up to
+  64 code bytes and 12 scale bytes past its end.  Those bytes only feed products whose
+  scales are zeroed, but they must be mapped: this is an open bound, not a guarantee.
+* The planned fix moves the column offset into the resource base and out of num_records,
+  saturating at zero; the model checks it keeps every fetch inside, and that a count
+  which wraps round instead admits the sentinel offset (2 GiB past the operand).
 """
 import numpy as np
 import pytest
@@ -123,13 +123,25 @@ SHAPES = [(1, 1, 128), (64, 96, 256), (300, 260, 384), (256, 512, 1024), (1100, 
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_every_fetched_byte_is_inside_its_operand(M, N, K):
-    tail = K % (2 * BKP) != 0                   # the launcher's choice of path
-    top = _fetched_max(M, N, K, tail)
+def test_fetches_of_the_kernel_as_built(M, N, K):
+    """The kernel as built (column offset in the SGPR offset for every K)."""
+    top = _fetched_max(M, N, K, tail=False)
+    size = _sizes(M, N, K)
+    assert top["a"] >= size["a"] and top["b"] >= size["b"]   # the last row is read whole
+    if K % (2 * BKP) == 0:
+        for key in top:
+            assert top[key] <= size[key], (key, top[key], size[key])
+    else:
+        over = {k: top[k] - size[k] for k in top}
+        assert max(over["a"], over["b"]) <= 64 and max(over["sa"], over["sb"]) <= 12, over
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_planned_fix_keeps_every_fetch_inside(M, N, K):
+    top = _fetched_max(M, N, K, tail=K % (2 * BKP) != 0)
     size = _sizes(M, N, K)
     for key in top:
         assert top[key] <= size[key], (key, top[key], size[key])
-    assert top["a"] == size["a"] and top["b"] == size["b"]   # and the last row is read whole
 
 
 def test_a_wrapping_resource_count_would_admit_the_sentinel():
@@ -143,9 +155,9 @@ def test_a_wrapping_resource_count_would_admit_the_sentinel():
     assert top["a"] == 64 and top["b"] == 64
 
 
-def test_sgpr_column_offset_would_overrun_on_a_ragged_k():
-    """The first scheme on K = 384 (a half last buffer): the last row's second half-buffer
-    is admitted by the VGPR check and fetched past the end of the operand."""
+def test_ragged_k_overrun_of_the_kernel_as_built():
+    """K = 384 (a half last buffer): the last row's second half-buffer is admitted by the
+    VGPR check and fetched past the end of the operand; the planned fix does not."""
     M, N, K = 300, 260, 384
     top = _fetched_max(M, N, K, tail=False)
     size = _sizes(M, N, K)
