@@ -301,6 +301,70 @@ def run_w4a4_gemm(args):
     return out
 
 
+def run_w4a4_fused(args):
+    """The fused-quantization experiment against the library's two-launch step, on the W4A4
+    configuration and the same rotating activation batches: fp4probe_gemm_fused_a (each
+    tile rotates and quantizes its bf16 A rows into LDS) versus fp4_quantize + fp4_gemm.
+    Both produce the same C; the line's value is the fused kernel's throughput."""
+    import ctypes
+    L = _probe_lib()
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.fp4probe_gemm_fused_a.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, vp]
+    wl = W.WORKLOADS["w4a4_gemm"]
+    M, K = wl.shape
+    N = wl.extra["N"]
+    a0 = W.gemm_activations((M, K), wl.seed).to(DEV)
+    n_a = max(2, -(-(1 << 30) // (M * K * 2)))
+    a_sets = [a0] + [torch.roll(a0, shifts=977 * i, dims=0) for i in range(1, n_a)]
+    w = W.gemm_weights(N, K, wl.extra["weight_seed"], wl.extra["weight_std"]).to(DEV)
+    b_codes, b_scales, _ = fp4.fp4_quantize(w, "mxfp4", 32)
+    del w
+    a_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    a_scales = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    it = [0]
+
+    def two_launch():
+        a = a_sets[it[0] % n_a]
+        it[0] += 1
+        fp4.fp4_quantize(a, "mxfp4", 32, codes=a_codes, scales=a_scales)
+        fp4.fp4_gemm(a_codes, a_scales, b_codes, b_scales, c=c)
+
+    def fused():
+        a = a_sets[it[0] % n_a]
+        it[0] += 1
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if L.fp4probe_gemm_fused_a(vp(a.data_ptr()), vp(b_codes.data_ptr()), vp(b_scales.data_ptr()), M, N, K,
+                                   vp(c.data_ptr()), 1, st) != 0:
+            raise RuntimeError("fp4probe_gemm_fused_a failed")
+
+    res = {}
+    for name, fn in (("two_launch", two_launch), ("fused", fused)):
+        settle(fn, args.settle)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = Timer()
+        for _ in range(args.steps):
+            s = t.start()
+            fn()
+            t.stop(s)
+        torch.cuda.synchronize()
+        res[name] = t.mean_ms()
+    flops = 2.0 * M * N * K
+    tf = flops / (res["fused"] * 1e-3) / 1e12
+    return {"metric": METRIC, "value": tf, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": res["fused"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp4-e2m1/e8m0 (fp32 accumulate)", "data": "synthetic",
+            "config": {"workload": "w4a4_fused: Hadamard-32 MXFP4 quantization of A bf16 8192x8192 inside every "
+                                   "GEMM tile, then the W4A4 GEMM against 28672x8192 MXFP4 weights, bf16 out",
+                       "M": M, "N": N, "K": K},
+            "steps_ms": res, "fused_over_two_launch": res["fused"] / res["two_launch"],
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP4_PEAK_TFLOPS, "traffic": None, "kernel": "k_gemm<8,fused A>",
+                         "kernel_ms": res["fused"], "flop_per_launch": flops}}
+
+
 def run_arcquant_gemm(args):
     """ARCQuant augmented GEMM: residual quantization (MXFP4) + one K+S GEMM, against the
     same activation path without residual channels (S = 0) and a K GEMM."""
@@ -725,7 +789,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="w4a4_gemm",
-                    choices=sorted(W.WORKLOADS) + ["hbm_copy", "hbm_read", "mfma_peak", "format_study"])
+                    choices=sorted(W.WORKLOADS) + ["hbm_copy", "hbm_read", "mfma_peak", "format_study",
+                                                   "w4a4_fused"])
     ap.add_argument("--op", default="quant", choices=["quant", "dequant"],
                     help="memory workloads: time the forward op (quantize / pack) or its inverse")
     ap.add_argument("--settle", type=float, default=1.0,
@@ -744,7 +809,8 @@ def main():
         raise SystemExit("no GPU visible")
     fp4.lib()                                   # fail loudly if the HIP library is missing
     runners = {"w4a4_gemm": run_w4a4_gemm, "arcquant_gemm": run_arcquant_gemm, "format_study": run_format_study,
-               "hbm_copy": run_hbm_copy, "hbm_read": run_hbm_read, "mfma_peak": run_mfma_peak}
+               "hbm_copy": run_hbm_copy, "hbm_read": run_hbm_read, "mfma_peak": run_mfma_peak,
+               "w4a4_fused": run_w4a4_fused}
     out = runners.get(args.workload, run_memory_workload)(args)
     print(json.dumps(out), flush=True)
 

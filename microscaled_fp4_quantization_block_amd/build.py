@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4.so")
 SOURCES = ["api.cpp", "quant.hip", "pack.hip", "arcquant.hip", "gemm.hip"]
 PROBE_LIB = os.path.join(PKG, "libfp4probe.so")
-PROBE_SOURCES = ["probes.hip"]
+PROBE_SOURCES = ["probes.hip", "gemm_fused.hip"]
 ARCH = "gfx950"
 
 

@@ -174,7 +174,7 @@ PROBE_LIB = os.path.join(os.path.dirname(B.library_path()), "libfp4probe.so")
 def test_probe_library_exports_its_header_and_rejects_bad_arguments():
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fp4probe_[a-z_]+)\s*\(", text)))
-    assert names == ["fp4probe_hbm_read", "fp4probe_mfma_loop"]
+    assert names == ["fp4probe_gemm_fused_a", "fp4probe_hbm_read", "fp4probe_mfma_loop"]
     L = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(L, n)
@@ -184,3 +184,9 @@ def test_probe_library_exports_its_header_and_rejects_bad_arguments():
     assert L.fp4probe_hbm_read(FAKE, 1000, FAKE, 4, None) == 1      # not a multiple of 16
     assert L.fp4probe_mfma_loop(10, 3, 4, FAKE, None) == 1            # unknown operand mode
     assert L.fp4probe_mfma_loop(10, 0, 0, FAKE, None) == 1
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.fp4probe_gemm_fused_a.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_int, vp]
+    assert L.fp4probe_gemm_fused_a(FAKE, FAKE, FAKE, 4, 4, 384, FAKE, 1, None) == 1   # K % 256 != 0
+    assert L.fp4probe_gemm_fused_a(None, FAKE, FAKE, 4, 4, 256, FAKE, 1, None) == 1
+    assert L.fp4probe_gemm_fused_a(FAKE + 8, FAKE, FAKE, 4, 4, 256, FAKE, 1, None) == 1
+    assert L.fp4probe_gemm_fused_a(None, None, None, 0, 4, 256, None, 1, None) == 0  # empty: no-op

@@ -5,7 +5,7 @@ own flags (no GPU needed):
   global -> LDS loads from inline assembly whose descriptor operand is constrained to
   scalar registers; a descriptor the compiler computes in vector registers still fills
   that operand, and the load then runs on whatever the encoding points at;
-* no kernel spills to scratch;
+* no kernel spills to scratch (the fused-quantization experiment excepted);
 * no packed fp32 arithmetic (v_pk_add_f32 / v_pk_mul_f32 / v_pk_fma_f32) in device code.
 """
 import os
@@ -69,8 +69,15 @@ def test_buffer_descriptors_are_scalar(isa):
     assert n > 0
 
 
+#: the fused-quantization experiment keeps the activation quantization's registers beside
+#: the GEMM's 128 accumulators per lane and spills; its measurement includes that traffic
+SPILL_ALLOWED = {"gemm_fused.hip"}
+
+
 def test_no_scratch(isa):
     for src, text in isa.items():
+        if src in SPILL_ALLOWED:
+            continue
         sizes = [int(v) for v in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
         assert sizes and max(sizes) == 0, f"{src}: a kernel uses {max(sizes)} bytes of scratch"
 
