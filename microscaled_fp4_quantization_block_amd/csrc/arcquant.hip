@@ -246,8 +246,8 @@ __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K,
   const uint32_t sb = nvfp4_block_scale_fast(absmax<16>(z), inv6s);
   const float sbv = e4m3_value(sb);
   const uint2 w = nvfp4_encode16_fast(z, recip_fast(sbv * s_t));
-  *reinterpret_cast<uint2*>(crow + 8 * b) = w;
-  srow[b] = (uint8_t)sb;
+  store_out(reinterpret_cast<uint2*>(crow + 8 * b), w);
+  store_out(srow + b, (uint8_t)sb);
   if (b < sblk) {
     float q[16];
     e2m1_decode8(w.x, 1.0f, q);
@@ -255,8 +255,8 @@ __device__ __forceinline__ void encode_block(const float (&z)[16], int b, int K,
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, z[i]);   // z - V s_b s_t
     const uint32_t sr = nvfp4_block_scale_fast(absmax<16>(q), inv6s);
-    *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t));
-    srow[nblk + b] = (uint8_t)sr;
+    store_out(reinterpret_cast<uint2*>(crow + K / 2 + 8 * b), nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t)));
+    store_out(srow + nblk + b, (uint8_t)sr);
   }
 }
 
@@ -274,8 +274,8 @@ __device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], floa
   const uint32_t sb = nvfp4_block_scale_fast(absmax<16>(x) * inv_rms, inv6s);
   const float sbv = e4m3_value(sb);
   const uint2 w = nvfp4_encode16_fast(x, inv_rms * recip_fast(sbv * s_t));
-  *reinterpret_cast<uint2*>(crow + 8 * b) = w;
-  srow[b] = (uint8_t)sb;
+  store_out(reinterpret_cast<uint2*>(crow + 8 * b), w);
+  store_out(srow + b, (uint8_t)sb);
   if (b < sblk) {
     // z = fl(x inv_rms) is formed here, not shared with the debug copy: shared, the
     // compiler hoists its 16 products above both branches into every block.
@@ -287,8 +287,8 @@ __device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], floa
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = fmaf(-(q[i] * sbv), s_t, x[i] * ir);   // z - V s_b s_t
     const uint32_t sr = nvfp4_block_scale_fast(absmax<16>(q), inv6s);
-    *reinterpret_cast<uint2*>(crow + K / 2 + 8 * b) = nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t));
-    srow[nblk + b] = (uint8_t)sr;
+    store_out(reinterpret_cast<uint2*>(crow + K / 2 + 8 * b), nvfp4_encode16_fast(q, recip_fast(e4m3_value(sr) * s_t)));
+    store_out(srow + nblk + b, (uint8_t)sr);
   }
 }
 
@@ -407,8 +407,8 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
     const uint32_t e = e8m0_from_amax(absmax<32>(z));
     const float sc = e8m0_value(e);
     const uint4 w = e2m1_encode32(z, sc);
-    *reinterpret_cast<uint4*>(crow + 16 * b) = w;
-    srow[b] = (uint8_t)e;
+    store_out(reinterpret_cast<uint4*>(crow + 16 * b), w);
+    store_out(srow + b, (uint8_t)e);
     if (b < sblk) {
       float q[32];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -417,8 +417,8 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
 #pragma unroll
       for (int i = 0; i < 32; ++i) q[i] = z[i] - q[i];
       const uint32_t er = e8m0_from_amax(absmax<32>(q));
-      *reinterpret_cast<uint4*>(crow + K / 2 + 16 * b) = e2m1_encode32(q, e8m0_value(er));
-      srow[nblk + b] = (uint8_t)er;
+      store_out(reinterpret_cast<uint4*>(crow + K / 2 + 16 * b), e2m1_encode32(q, e8m0_value(er)));
+      store_out(srow + nblk + b, (uint8_t)er);
     }
   }
 }

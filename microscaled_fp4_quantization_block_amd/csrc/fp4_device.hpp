@@ -75,6 +75,47 @@ __device__ __forceinline__ void store_bf16(uint16_t* p, const float* v) {
   }
 }
 
+// Output stores.  Codes, scales and dequantized values are written once and read, if at
+// all, by a later launch: non-temporal stores stream them out without allocating in L2 or
+// the Infinity Cache, where a write stream of a working set's size only evicts what the
+// loads still need (bf16 4096 x 4096 dequantization: 9.6 us -> 7.2 us).
+typedef unsigned int out_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int out_u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store_out(uint4* p, uint4 w) {
+  __builtin_nontemporal_store(out_u32x4{w.x, w.y, w.z, w.w}, reinterpret_cast<out_u32x4*>(p));
+}
+__device__ __forceinline__ void store_out(uint2* p, uint2 w) {
+  __builtin_nontemporal_store(out_u32x2{w.x, w.y}, reinterpret_cast<out_u32x2*>(p));
+}
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, T v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+template <int N>
+__device__ __forceinline__ void store_f32_out(float* p, const float* v) {
+  uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i)
+    store_out(q + i, make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                                __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])));
+}
+
+template <int N>
+__device__ __forceinline__ void store_bf16_out(uint16_t* p, const float* v) {
+  uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    uint4 w;
+    w.x = pack_bf16x2(v[8 * i + 0], v[8 * i + 1]);
+    w.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
+    w.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
+    w.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
+    store_out(q + i, w);
+  }
+}
+
 // --------------------------------------------------------------------------- Hadamard
 
 // Unnormalised Sylvester-ordered Walsh-Hadamard transform of v[0..N) in registers:

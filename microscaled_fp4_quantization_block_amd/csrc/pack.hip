@@ -48,15 +48,15 @@ k_pack(const uint16_t* x, int64_t nchunks, uint8_t* codes, uint8_t* micro, float
     sm[h] = nvfp4_block_scale_fast(absmax<16>(v + 16 * h), inv6s);
     w[h] = nvfp4_encode16_fast(v + 16 * h, recip_fast(e4m3_value(sm[h]) * s_g));
   }
-  reinterpret_cast<uint4*>(codes)[c] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
-  reinterpret_cast<uint16_t*>(micro)[c] = (uint16_t)(sm[0] | (sm[1] << 8));
-  if (p == 0) group[c >> 2] = s_g;
+  store_out(reinterpret_cast<uint4*>(codes) + c, make_uint4(w[0].x, w[0].y, w[1].x, w[1].y));
+  store_out(reinterpret_cast<uint16_t*>(micro) + c, (uint16_t)(sm[0] | (sm[1] << 8)));
+  if (p == 0) store_out(group + (c >> 2), s_g);
 }
 
 // Unpack by groups of 16 lanes: lane g of a group owns elements 8 g .. 8 g + 7 of one
 // 128-group (one 4-byte code word), so a wave's bf16 stores are 1 KiB contiguous; the
 // two-level FWHT finishes with DPP butterflies across the 16 lanes.
-constexpr int kUnpackUnits = 2;
+constexpr int kUnpackUnits = 4;
 
 __global__ void __launch_bounds__(kThreads)
 k_unpack(const uint8_t* codes, const uint8_t* micro, const float* group, int64_t n8, uint16_t* y) {
@@ -81,7 +81,7 @@ k_unpack(const uint8_t* codes, const uint8_t* micro, const float* group, int64_t
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (v[j] * smv) * sg[u];     // V s_m exact
     group16_two_level_fwht8(v, g);                               // every lane takes part
-    if (i < n8) store_bf16<8>(y + i * 8, v);
+    if (i < n8) store_bf16_out<8>(y + i * 8, v);
   }
 }
 

@@ -67,8 +67,8 @@ k_quant_mx(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales, floa
   chunk_rotate<H>(v, c);
   if (dbg) store_f32<32>(dbg + c * 32, v);
   uint32_t e = e8m0_from_amax(absmax<32>(v));
-  reinterpret_cast<uint4*>(codes)[c] = e2m1_encode32(v, e8m0_value(e));
-  scales[c] = (uint8_t)e;
+  store_out(reinterpret_cast<uint4*>(codes) + c, e2m1_encode32(v, e8m0_value(e)));
+  store_out(scales + c, (uint8_t)e);
 }
 
 // NVFP4: two 16-blocks per chunk.  Unrotated input takes the exact scale and element
@@ -105,8 +105,8 @@ k_quant_nv(const void* x, int64_t nchunks, uint8_t* codes, uint8_t* scales,
       w[b] = nvfp4_encode16_fast(v + 16 * b, recip_fast(e4m3_value(sb[b]) * s_t));
     }
   }
-  reinterpret_cast<uint4*>(codes)[c] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
-  reinterpret_cast<uint16_t*>(scales)[c] = (uint16_t)(sb[0] | (sb[1] << 8));
+  store_out(reinterpret_cast<uint4*>(codes) + c, make_uint4(w[0].x, w[0].y, w[1].x, w[1].y));
+  store_out(reinterpret_cast<uint16_t*>(scales) + c, (uint16_t)(sb[0] | (sb[1] << 8)));
 }
 
 // Dequantization: fl32(V s_b s_t) (NVFP4) or V 2^(e-127) (MXFP4), optional H, store.
@@ -144,9 +144,9 @@ k_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale
     unit_rotate8<H>(v, threadIdx.x);                            // every lane takes part
     if (i < n8) {
       if constexpr (OUT == fp4impl::DT_F32)
-        store_f32<8>(reinterpret_cast<float*>(y) + i * 8, v);
+        store_f32_out<8>(reinterpret_cast<float*>(y) + i * 8, v);
       else
-        store_bf16<8>(reinterpret_cast<uint16_t*>(y) + i * 8, v);
+        store_bf16_out<8>(reinterpret_cast<uint16_t*>(y) + i * 8, v);
     }
   }
 }
