@@ -13,7 +13,7 @@
 //   1. The row streams in with coalesced 16-byte loads (eight per lane in flight), its
 //      sum of squares accumulates in registers, and the raw bf16 row is parked in the
 //      wave's own LDS slice.
-//   2. A butterfly sum gives every lane the same sum, hence the same 1/rms.
+//   2. A DPP reduction gives every lane the same sum, hence the same 1/rms.
 //   3. Lane l then encodes blocks l, l + 64, ...: the 16 channel indices of a block come
 //      from the permutation, staged once per workgroup in LDS as 16-bit byte offsets into the
 //      row (2 c, below 2^15 for K <= 16384; one SDWA add forms each address), and the
@@ -102,7 +102,7 @@ __device__ __forceinline__ float park_units(const uint4 (&raw)[kUnroll], int u0,
 }
 
 // Stream one row: sum of squares in a fixed order (lane-local over its units, then a
-// butterfly), raw bf16 parked at xs.  Identical arithmetic in every pass.
+// wave reduction), raw bf16 parked at xs.  Identical arithmetic in every pass.
 __device__ __forceinline__ float load_row(const uint16_t* __restrict__ xr, int units, int lane, uint16_t* xs) {
   float ss = 0.0f;
   for (int u0 = 0; u0 < units; u0 += 64 * kUnroll) {
@@ -113,8 +113,10 @@ __device__ __forceinline__ float load_row(const uint16_t* __restrict__ xr, int u
   return wave_sum(ss);
 }
 
+// 1 / sqrt(ss / K + eps): one fused multiply-add and the hardware reciprocal square root
+// (v_rsq_f32, within 1 ulp), well inside the tolerance the normalised values are held to.
 __device__ __forceinline__ float inv_rms_of(float ss, int K, float eps) {
-  return 1.0f / sqrtf(ss / (float)K + eps);
+  return __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / (float)K, eps));
 }
 
 // z = fl(x / rms), times the channel's gamma value g when the norm has a gain (kGamma):
@@ -177,7 +179,7 @@ k_arc_stats(const uint16_t* __restrict__ x, int64_t M, int K, const float* __res
 
 // Statistics pass for rows of at most 64 kUnroll units: rows stay in registers (no LDS
 // copy), two per wave per step with both rows' loads in flight.  The sum of squares takes
-// the same per-lane order as park_units and the same butterfly, so 1/rms is the
+// the same per-lane order as park_units and the same wave reduction, so 1/rms is the
 // quantizing pass's to the bit.  Without a gain vector the row's max|z| is max|x| times
 // 1/rms, which by monotone rounding equals the maximum of the rounded products; with one,
 // every element's fl(fl(x / rms) g) is formed as norm_value does.

@@ -552,10 +552,26 @@ __device__ __forceinline__ float wave_max(float m) {
   return m;
 }
 
-__device__ __forceinline__ float wave_sum(float s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  return s;
+// One DPP step: v plus the value of the lane that dpp_ctrl kCtrl selects.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the wave, the same value in every lane, in a fixed order: partner sums within
+// each row of 16 lanes by DPP (lane ^ 1, lane ^ 2, the half-row mirror, the row mirror --
+// each pairs every lane with one partner, and a + b = b + a, so the lanes of a row agree),
+// then (row 0 + row 1) + (row 2 + row 3) from lanes 0, 16, 32, 48.  No LDS round trip.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);   // row_half_mirror
+  v = dpp_add<0x140>(v);   // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Running maximum of non-negative floats through their bit patterns (monotone for >= 0).
