@@ -494,9 +494,12 @@ def run_format_study(args):
             "data": "synthetic", "config": {"workload": "format_study"}, "errors": table}
 
 
+def _rotating_count(nbytes_per_set, min_total=1 << 30):
+    return range(max(2, -(-min_total // max(nbytes_per_set, 1))))
+
+
 def _rotating(make, nbytes_per_set, min_total=1 << 30):
-    sets = max(2, -(-min_total // max(nbytes_per_set, 1)))
-    return [make() for _ in range(sets)]
+    return [make() for _ in _rotating_count(nbytes_per_set, min_total)]
 
 
 def run_hbm_copy(args):
@@ -627,13 +630,11 @@ def _memory_case(name, op):
     raise SystemExit(f"unknown workload {name}")
 
 
-def run_memory_workload(args):
-    """K launches over rotating buffer sets, captured once into a HIP graph so that the
-    host's launch cost does not pace these short kernels; the timed region is one replay
-    bracketed by one HIP event pair on the replay stream."""
-    name, op = args.workload, args.op
-    wl = W.WORKLOADS[name]
-    make, launch, nbytes, kernel, cpu = _memory_case(name, op)
+def _memory_pass(args, make, launch, nbytes):
+    """One measurement: fresh rotating buffer sets, the settle phase, warmup launches, then
+    `steps` launches captured into one HIP graph; after an untimed replay (which uploads the
+    graph) one replay is timed with a HIP event pair on the replay stream.  Returns
+    (mean ms per launch, wall seconds of the timed replay, settle record)."""
     sets = _rotating(make, nbytes)
     i = [0]
 
@@ -649,7 +650,7 @@ def run_memory_workload(args):
     with torch.cuda.graph(g):
         for k in range(args.steps):
             launch(sets[k % len(sets)])
-    g.replay()                                   # untimed: first replay uploads the graph
+    g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -658,7 +659,25 @@ def run_memory_workload(args):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kms = e0.elapsed_time(e1) / args.steps
+    del g, sets
+    return e0.elapsed_time(e1) / args.steps, wall, settled
+
+
+def run_memory_workload(args):
+    """K launches over rotating buffer sets, captured once into a HIP graph so that the
+    host's launch cost does not pace these short kernels; the timed region is one replay
+    bracketed by one HIP event pair on the replay stream.
+
+    The whole measurement runs twice and the second is reported: the first pass of a
+    process over freshly allocated buffers can be slower (the dual-scale unpack measured
+    33.6-38.3 us on its first pass against 29.9-31.1 us on later ones, in the same process,
+    on the same sizes), which is a property of the process's first allocations, not of the
+    kernel.  The first pass's figure is reported beside it (`first_pass_kernel_ms`)."""
+    name, op = args.workload, args.op
+    wl = W.WORKLOADS[name]
+    make, launch, nbytes, kernel, cpu = _memory_case(name, op)
+    first_kms, _, _ = _memory_pass(args, make, launch, nbytes)
+    kms, wall, settled = _memory_pass(args, make, launch, nbytes)
     gbs = nbytes / (kms * 1e-3) / 1e9
     out = {"metric": METRIC, "value": nbytes * args.steps / wall / 1e9, "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
@@ -669,8 +688,10 @@ def run_memory_workload(args):
            "settle": settled,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(f"{name}_{op}"), "kernel": kernel,
-                        "kernel_ms": kms, "bytes_per_launch": nbytes, "buffer_sets": len(sets),
-                        "timing": "one HIP event pair around a graph replay of `steps` launches"}}
+                        "kernel_ms": kms, "first_pass_kernel_ms": first_kms, "bytes_per_launch": nbytes,
+                        "buffer_sets": len(_rotating_count(nbytes)),
+                        "timing": "one HIP event pair around a graph replay of `steps` launches, "
+                                  "second of two passes"}}
     if not args.no_cpu:
         oname, chunk, rows, what = cpu
         out["cpu_baseline"] = cpu_baseline_rows(oname, chunk, rows, nbytes / wl.shape[0], what)

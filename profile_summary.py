@@ -56,7 +56,7 @@ CASES = {
               "k_gemm MXFP4 8192x28672x8192, bf16 out (one extra k_quant_mx dispatch quantizes the 28672x8192 "
               "weights, and the settle phase repeats the step for a second before the timed steps)",
         bench=["--workload", "w4a4_gemm"], steps=20, timed=20, pmc=[SQ_PASS],
-        kernels={"k_gemm": ("gemm_w4a4", ["gemm.hip"] + DEVICE_HPP, 630194176, 2.0 * M_ * N_ * K_),
+        kernels={"k_gemm": ("gemm_w4a4", ["gemm.hip", "gemm_core.hpp"] + DEVICE_HPP, 630194176, 2.0 * M_ * N_ * K_),
                  "k_quant_mx": ("quant_mx_h32_a", ["quant.hip"] + DEVICE_HPP, 169869312, None)}),
     "k_quant_mx_h32_4096x4096": dict(
         title="Hadamard-32 MXFP4 quantization, bf16 4096x4096 with 41 outlier channels x50 (rotating buffers)",
@@ -90,6 +90,14 @@ CASES = {
               "the same step at S = 0 (k_gemm 4096x14336x4096)",
         bench=["--workload", "arcquant_gemm"], steps=20, timed=None, pmc=[],
         kernels={"k_gemm": (None, [], None, None), "k_arcquant": (None, [], None, None)}),
+    "w4a4_fused_8192x28672x8192": dict(
+        title="fused-quantization experiment: k_gemm<8, true> (each tile rotates and quantizes its bf16 A "
+              "rows into LDS) against the two-launch step k_quant_mx<bf16,H32> + k_gemm<8, false>, W4A4 "
+              "8192x28672x8192",
+        bench=["--workload", "w4a4_fused"], steps=5, timed=None, pmc=[],
+        kernels={"k_gemm<8, true>": (None, [], None, 2.0 * M_ * N_ * K_),
+                 "k_gemm<8, false>": (None, [], None, 2.0 * M_ * N_ * K_),
+                 "k_quant_mx": (None, [], None, None)}),
     "hbm_read_1GiB": dict(
         title="roofline probe: read-only HBM stream, 1 GiB per launch", bench=["--workload", "hbm_read"],
         steps=20, timed=20, pmc=[], kernels={"k_hbm_read": (None, [], 1 << 30, None)}),
@@ -276,8 +284,10 @@ def summarize(name, out):
             g = v.get("GRBM_GUI_ACTIVE")
             if g:
                 g /= XCDS                      # cycles per XCD: the kernel's length in shader cycles
-                lines.append(f"    GRBM_GUI_ACTIVE / {XCDS} XCDs = {g:.0f} cycles in {v['_duration_ns'] / 1e3:.1f} us "
-                             f"-> shader clock {g / v['_duration_ns']:.2f} GHz during this (serialised) dispatch")
+                clk = (f"-> shader clock {g / v['_duration_ns']:.2f} GHz during this (serialised) dispatch"
+                       if v["_duration_ns"] >= 200e3 else
+                       "(dispatch too short for a clock estimate: the active span includes its start and drain)")
+                lines.append(f"    GRBM_GUI_ACTIVE / {XCDS} XCDs = {g:.0f} cycles in {v['_duration_ns'] / 1e3:.1f} us {clk}")
             if g and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
                 lines.append(f"    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {SIMDS} SIMDs) = "
                              f"{100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * SIMDS):.1f} %")
