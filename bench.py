@@ -147,7 +147,9 @@ def _oracle_op(name, data):
     elif name == "dualscale_pack_dequant":
         two_level_128(dualscale.dequantized(*data))
     elif name == "arcquant_quant":
-        arcquant.quantize(data[0], data[1], data[2], tensor_scale_value=data[3])
+        arcquant.quantize(data[0], data[1], data[2], gamma=data[4], tensor_scale_value=data[3])
+    elif name == "arcquant_mx_quant":
+        arcquant.quantize_mx(data[0], data[1], data[2], gamma=data[4])
     elif name == "nvfp4_roundtrip_quant":
         q = nvfp4.quantize(data[0])
         nvfp4.dequantize(q["packed"], q["scales"], q["tensor_scale"])
@@ -586,28 +588,42 @@ def _memory_case(name, op):
         cpu = ("dualscale_pack_dequant", lambda lo, hi: (codes[lo:hi], sm[lo:hi], sg[lo:hi]), 1024,
                "oracle two-level FWHT of dualscale.dequantized (rows of the first 1024)")
         return make, launch, nbytes, "k_unpack", cpu
-    if name == "arcquant":
+    if name in ("arcquant", "arcquant_gamma", "arcquant_mx"):
         if op != "quant":
-            raise SystemExit("arcquant has no inverse op")
+            raise SystemExit(f"{name} has no inverse op")
+        mx = name == "arcquant_mx"
         x_cpu = W.arcquant_input(wl.shape, wl.seed)
         S = wl.extra["S"]
         perm_np = W.calibration_order(x_cpu)
         perm = torch.from_numpy(perm_np).to(DEV)
-        ts = torch.zeros(1, dtype=torch.float32, device=DEV)
-        fp4.fp4_residual_quantize(x_cpu.to(DEV), perm, S, tensor_scale=ts)        # calibrate once
-        nbytes = M * K * 2 + K * 4 + M * (K + S) // 2 + M * (K + S) // 16 + 4
+        g_np = W.arcquant_gain(K, wl.extra["gamma_seed"]) if "gamma_seed" in wl.extra else None
+        gamma = torch.from_numpy(g_np).to(DEV) if g_np is not None else None
+        sdiv = 32 if mx else 16
+        nbytes = M * K * 2 + K * 4 + M * (K + S) // 2 + M * (K + S) // sdiv + (0 if mx else 4)
+        nbytes += 4 * K if gamma is not None else 0
         xv = W.values(x_cpu)
-        st = np.float32(ts.cpu().numpy()[0])
 
         def make():
             return (x_cpu.to(DEV), torch.empty((M, (K + S) // 2), dtype=torch.uint8, device=DEV),
-                    torch.empty((M, (K + S) // 16), dtype=torch.uint8, device=DEV))
+                    torch.empty((M, (K + S) // sdiv), dtype=torch.uint8, device=DEV))
+
+        if mx:
+            def launch(s):
+                fp4.fp4_residual_quantize_mx(s[0], perm, S, gamma=gamma, codes=s[1], scales=s[2])
+            cpu = ("arcquant_mx_quant", lambda lo, hi: (xv[lo:hi], perm_np, S, None, g_np), M,
+                   "oracle arcquant.quantize_mx")
+            return make, launch, nbytes, "k_arcquant<MXFP4>", cpu
+        ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+        fp4.fp4_residual_quantize(x_cpu.to(DEV), perm, S, gamma=gamma, tensor_scale=ts)   # calibrate once
+        st = np.float32(ts.cpu().numpy()[0])
 
         def launch(s):
-            fp4.fp4_residual_quantize(s[0], perm, S, codes=s[1], scales=s[2], tensor_scale=ts, mode="given")
-        cpu = ("arcquant_quant", lambda lo, hi: (xv[lo:hi], perm_np, S, st), M,
-               "oracle arcquant.quantize with the calibrated tensor scale")
-        return make, launch, nbytes, "k_arcquant<NVFP4> (static tensor scale)", cpu
+            fp4.fp4_residual_quantize(s[0], perm, S, gamma=gamma, codes=s[1], scales=s[2], tensor_scale=ts,
+                                      mode="given")
+        with_g = " and the gain vector" if g_np is not None else ""
+        cpu = ("arcquant_quant", lambda lo, hi: (xv[lo:hi], perm_np, S, st, g_np), M,
+               "oracle arcquant.quantize with the calibrated tensor scale" + with_g)
+        return make, launch, nbytes, "k_arcquant<NVFP4> (static tensor scale)" + with_g, cpu
     if name == "nvfp4_roundtrip":
         if op != "quant":
             raise SystemExit("nvfp4_roundtrip times quantize + dequantize together")

@@ -50,6 +50,16 @@ WORKLOADS = {
         "fused RMSNorm + absmax channel reorder + NVFP4 primary + residual of top 256 "
         "channels: bf16 4096x4096 N(0,1), 64 outlier channels x30, K+S = 4352",
         (4096, 4096), 4, dict(outliers=64, outlier_gain=30.0, S=256, eps=1e-6)),
+    "arcquant_gamma": Workload(
+        "arcquant_gamma",
+        "the arcquant workload with a gain vector: gamma[K] uniform in [0.5, 1.5] (seed 7), "
+        "NVFP4 primary + residual of top 256 channels, K+S = 4352",
+        (4096, 4096), 4, dict(outliers=64, outlier_gain=30.0, S=256, eps=1e-6, gamma_seed=7)),
+    "arcquant_mx": Workload(
+        "arcquant_mx",
+        "the arcquant workload in the MXFP4 flavour: RMSNorm + reorder + MXFP4 primary + "
+        "residual of top 256 channels, E8M0 per 32, K+S = 4352",
+        (4096, 4096), 4, dict(outliers=64, outlier_gain=30.0, S=256, eps=1e-6)),
     "arcquant_gemm": Workload(
         "arcquant_gemm",
         "ARCQuant augmented GEMM (MXFP4 flavour): bf16 4096x4096 activations N(0,1) with 64 "
@@ -104,6 +114,11 @@ def student_t_input(shape=(8192, 8192), seed=3, df=4):
 
 def arcquant_input(shape=(4096, 4096), seed=4, outliers=64, gain=30.0):
     return to_bf16(gaussian_with_outliers(shape, seed, outliers, gain))
+
+
+def arcquant_gain(k, seed=7):
+    """A seeded RMSNorm gain vector, float32 [k], uniform in [0.5, 1.5]."""
+    return np.random.default_rng(seed).uniform(0.5, 1.5, k).astype(np.float32)
 
 
 def calibration_order(x):

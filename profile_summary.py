@@ -79,6 +79,15 @@ CASES = {
               "static tensor scale (rotating buffers)",
         bench=["--workload", "arcquant"], steps=100, timed=100, pmc=[SQ_PASS],
         kernels={"k_arcquant": ("arcquant_quant", ["arcquant.hip"] + DEVICE_HPP, 43597828, None)}),
+    "k_arcquant_gamma_4096x4096_S256": dict(
+        title="ARCQuant NVFP4 with a gain vector (gamma uniform in [0.5, 1.5]), S = 256, bf16 4096x4096, "
+              "static tensor scale (rotating buffers)",
+        bench=["--workload", "arcquant_gamma"], steps=100, timed=100, pmc=[SQ_PASS],
+        kernels={"k_arcquant": ("arcquant_gamma_quant", ["arcquant.hip"] + DEVICE_HPP, 43614212, None)}),
+    "k_arcquant_mx_4096x4096_S256": dict(
+        title="ARCQuant MXFP4 flavour (E8M0 per 32), S = 256, bf16 4096x4096 (rotating buffers)",
+        bench=["--workload", "arcquant_mx"], steps=100, timed=100, pmc=[SQ_PASS],
+        kernels={"k_arcquant": ("arcquant_mx_quant", ["arcquant.hip"] + DEVICE_HPP, 43040768, None)}),
     "nvfp4_roundtrip_256x1024": dict(
         title="NVFP4 quantize + dequantize round trip, fp32 256x1024, dynamic tensor scale",
         bench=["--workload", "nvfp4_roundtrip"], steps=100, timed=100, pmc=[],
