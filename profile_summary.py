@@ -6,7 +6,7 @@ Two steps, because the GPU run and the summary may happen on different machines:
       On a machine with the GPU: runs bench.py under rocprofv3 as child processes, one
       pass each -- the kernel trace with statistics, then FETCH_SIZE, then WRITE_SIZE, then
       the named profile's extra counter sets -- writing raw CSV under DIR/NAME (default
-      gpurun_out/prof).  Each pass runs under its own time limit; the first failure stops
+      rocprof_out).  Each pass runs under its own time limit; the first failure stops
       the sequence.  This script itself never touches the GPU.
 
   python3 profile_summary.py summarize NAME [--out DIR]
@@ -241,7 +241,7 @@ def summarize(name, out):
     d = os.path.join(out, name)
     kernels = c["kernels"]
     lines = [f"# {c['title']}", "", "Commands (from the repository root, with TMPDIR=/tmp):"]
-    lines += ["  " + _display(cmd) for _, _, cmd in _commands(name, os.path.join("gpurun_out", "prof"))]
+    lines += ["  " + _display(cmd) for _, _, cmd in _commands(name, "rocprof_out")]
     durs = _trace(os.path.join(d, "trace"), kernels, c["timed"])
     lines += ["", "Kernel durations from the kernel trace (microseconds):",
               f"  {'kernel':28s} {'dispatches':>10s} {'avg':>9s} {'min':>9s} {'max':>9s}   "
@@ -328,7 +328,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("action", choices=["run", "summarize", "list"])
     ap.add_argument("names", nargs="*")
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "rocprof_out"))
     a = ap.parse_args()
     if a.action == "list":
         print("\n".join(CASES))
