@@ -40,3 +40,28 @@ def test_default_run_prints_the_contract_line():
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
+
+
+MEMORY_WORKLOADS = [("mxfp4_h32", "quant"), ("mxfp4_h32", "dequant"), ("dualscale_pack", "quant"),
+                    ("dualscale_pack", "dequant"), ("arcquant", "quant"), ("arcquant_gamma", "quant"),
+                    ("arcquant_mx", "quant"), ("nvfp4_roundtrip", "quant")]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("workload,op", MEMORY_WORKLOADS)
+def test_memory_workload_lines(workload, op):
+    """Each memory-bound workload prints one contract line with its HBM roofline, timed on
+    the second of two passes, the first pass reported beside it."""
+    print(f"bench.py --workload {workload} --op {op}", flush=True)
+    p = _bench("--workload", workload, "--op", op, "--steps", "5", "--warmup", "1", "--settle", "0.2",
+               "--no-cpu", timeout=240)
+    assert p.returncode == 0, p.stderr[-2000:]
+    lines = [l for l in p.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["achieved"] > 0
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
+    assert r["kernel_ms"] > 0 and r["first_pass_kernel_ms"] > 0 and r["bytes_per_launch"] > 0
+    assert abs(r["achieved"] - r["bytes_per_launch"] / (r["kernel_ms"] * 1e-3) / 1e9) < 1e-6 * r["achieved"]
+    assert workload in d["config"]["workload"]
