@@ -86,3 +86,19 @@ def test_no_packed_fp32(isa):
     for src, text in isa.items():
         bad = [i for i in _instructions(text) if re.match(r"v_pk_(add|mul|fma)_f32\b", i)]
         assert not bad, f"{src}: {bad[:3]}"
+
+
+def test_m0_only_around_the_lds_dma(isa):
+    """The GEMM's global -> LDS loads set M0 inside their own asm statement and list it as
+    clobbered.  M0 is a register the compiler reserves, so it does not promise to keep a
+    value of its own in M0 across such a statement: check that no compiler-generated
+    instruction uses M0 at all, i.e. every M0 reference is an asm `s_mov_b32 m0, ...`
+    directly followed by its `s_nop 0` and the `buffer_load ... lds`."""
+    for src, text in isa.items():
+        ins = list(_instructions(text))
+        for i, line in enumerate(ins):
+            if not re.search(r"\bm0\b", line):
+                continue
+            assert line.startswith("s_mov_b32 m0,"), f"{src}: compiler use of M0: '{line}'"
+            assert ins[i + 1] == "s_nop 0" and re.match(r"buffer_load_dwordx4 .* lds$", ins[i + 2]), \
+                f"{src}: M0 write not followed by its LDS DMA: {ins[i:i + 3]}"
