@@ -185,11 +185,11 @@ fp4_status fp4_unpack(const void* packed, int64_t M, int64_t K, void* y, void* s
  *   a_codes [M][K/2], a_scales [M][K/32], b_codes [N][K/2], b_scales [N][K/32],
  *   c [M][N] in ct (FP4_BF16: nearest-even from the fp32 sum; FP4_F32).
  * Shapes: M, N >= 0, K > 0, K % 128 == 0, M*K/2 and N*K/2 below 2^31 bytes.
- * Reads past the operands when K % 512 != 0: the last 256-element step of a row is
+ * Reads past the operands when K % 256 == 128: the last 256-element step of a row is
  * fetched whole, so at the last row of each operand up to 64 bytes past the end of
- * a_codes / b_codes and up to 12 bytes past the end of a_scales / b_scales are read
- * (never written, and their products are zeroed).  The caller must leave that much
- * readable memory after each operand; for K % 512 == 0 nothing outside is read.
+ * a_codes / b_codes are read (never written; those products are zeroed).  The caller must
+ * leave that much readable memory after each code operand.  For K % 256 == 0 nothing
+ * outside the operands is read; scales are never read past their end.
  */
 fp4_status fp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, fp4_dtype ct,

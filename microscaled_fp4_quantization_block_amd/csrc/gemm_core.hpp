@@ -169,15 +169,17 @@ __device__ __forceinline__ void issue_codes(const Loader<NW, FA>& L, int p, bool
 // Issue scale group h (16 scale bytes per row: K elements 512 h .., counted from the
 // tile's starting buffer) into `dst` ([A rows][16 B] then [B rows][16 B]); instruction t
 // covers rows 64 (t % 4) + l of operand t / 4.  rot is even, so a group never straddles
-// the wrap.
+// the wrap.  The group's column goes into the VGPR offset, which the descriptor's range
+// check covers: when K % 512 != 0 the last group is half a group, and at the operand's
+// last row its second 8 bytes lie past the end; they read as zeros (and are never used).
 template <int NW, bool FA>
 __device__ __forceinline__ void issue_scales(const Loader<NW, FA>& L, int h, bool valid, uint8_t* dst) {
-  const int soff = (rotated(L, 2 * h) >> 1) * kScaleRow;
+  const uint32_t col = (uint32_t)((rotated(L, 2 * h) >> 1) * kScaleRow);
 #pragma unroll
   for (int q = 0; q < Loader<NW, FA>::SW; ++q) {
     const int t = Loader<NW, FA>::SW * L.wave + q;
     uint8_t* blk = dst + (t >> 2) * kScaleBytes + (t & 3) * 1024;
-    if (!FA || (t >> 2)) dma16((t >> 2) ? L.rSB : L.rSA, blk, valid ? L.scale_off[q] : kOOB, soff);
+    if (!FA || (t >> 2)) dma16((t >> 2) ? L.rSB : L.rSA, blk, (valid ? L.scale_off[q] : kOOB) + col, 0u);
   }
 }
 

@@ -8,12 +8,13 @@ the scale groups, every issue including those past the end of K with their out-o
 sentinel), assumes the check admits a dword when VGPR offset + 4 <= num_records, and
 compares the admitted dwords' addresses with the operand's size.
 
-* K % 512 == 0: every code buffer ends by column K / 2 and every scale group by K / 32, so
-  nothing leaves its row: every fetched byte is inside the operand.
-* Otherwise (a half last buffer, or a half last scale group) the last buffer's chunks past
-  a row's end are admitted and read the next row, and at the operand's last row up to
-  64 code bytes and 12 scale bytes past its end.  Those bytes only feed products whose
-  scales are zeroed, but they must be mapped: this is an open bound, not a guarantee.
+* The scale loads carry their column in the VGPR offset, so the range check covers it: a
+  half last scale group (K % 512 != 0) reads zeros past the operand's last row.
+* K % 256 == 0: every code buffer ends by column K / 2, so nothing leaves the operand.
+* K % 256 == 128 (a half last buffer): the last buffer's chunks past a row's end are
+  admitted and read the next row, and at the operand's last row up to 64 code bytes past
+  its end.  Those bytes only feed products whose scales are zeroed, but they must be
+  mapped: this is an open bound, not a guarantee.
 * The planned fix moves the column offset into the resource base and out of num_records,
   saturating at zero; the model checks it keeps every fetch inside, and that a count
   which wraps round instead admits the sentinel offset (2 GiB past the operand).
@@ -64,10 +65,11 @@ def _issues(np_):
     return codes, scales
 
 
-def _fetched_max(M, N, K, tail, wrap=False):
+def _fetched_max(M, N, K, tail, wrap=False, scale_col_in_voff=True):
     """Largest byte offset + 1 fetched from each operand (A codes, B codes, A scales,
     B scales) over every tile and issued load, or -1 if none.  `wrap` models a resource
-    count that wraps round instead of saturating when the column exceeds it."""
+    count that wraps round instead of saturating when the column exceeds it;
+    `scale_col_in_voff` the scale loads' column in the VGPR offset (as built)."""
     rowbytes, rowscales = K // 2, K // 32
     np_ = (K + BKP - 1) // BKP
     tiles_m, tiles_n = (M + BM - 1) // BM, (N + BN - 1) // BN
@@ -75,7 +77,14 @@ def _fetched_max(M, N, K, tail, wrap=False):
     code_issues, scale_issues = _issues(np_)
     top = {"a": -1, "b": -1, "sa": -1, "sb": -1}
 
-    def admit(key, base, nrec, col, voff, valid):
+    def admit(key, base, nrec, col, voff, valid, col_in_voff=False):
+        if col_in_voff:
+            voff = (np.asarray(voff, dtype=np.int64) if valid else np.full(64, KOOB, dtype=np.int64)) + col
+            for d in range(4):
+                ok = voff + 4 * d + 4 <= nrec
+                if ok.any():
+                    top[key] = max(top[key], int(base + voff[ok].max() + 4 * d + 4))
+            return
         if tail:
             base, soff = base + col, 0
             nrec = (nrec - col) % (1 << 32) if wrap else max(nrec - col, 0)
@@ -109,7 +118,8 @@ def _fetched_max(M, N, K, tail, wrap=False):
                     for i in range(SW):
                         t = SW * wave + i
                         key, r0, rows = ("sb", n0, rows_b) if t >> 2 else ("sa", m0, rows_a)
-                        admit(key, r0 * rowscales, rows * rowscales, col, scale_off[wave][i], valid)
+                        admit(key, r0 * rowscales, rows * rowscales, col, scale_off[wave][i], valid,
+                              col_in_voff=scale_col_in_voff and not tail)
     return top
 
 
@@ -122,18 +132,27 @@ SHAPES = [(1, 1, 128), (64, 96, 256), (300, 260, 384), (256, 512, 1024), (1100, 
           (513, 257, 8192), (130, 70, 640), (200, 300, 1408), (300, 600, 8192)]
 
 
-@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("M,N,K", SHAPES + [(256, 256, 4352), (300, 260, 4352)])
 def test_fetches_of_the_kernel_as_built(M, N, K):
-    """The kernel as built (column offset in the SGPR offset for every K)."""
+    """The kernel as built: code loads with the column in the SGPR offset, scale loads with
+    it in the VGPR offset."""
     top = _fetched_max(M, N, K, tail=False)
     size = _sizes(M, N, K)
     assert top["a"] >= size["a"] and top["b"] >= size["b"]   # the last row is read whole
-    if K % (2 * BKP) == 0:
-        for key in top:
-            assert top[key] <= size[key], (key, top[key], size[key])
+    assert top["sa"] <= size["sa"] and top["sb"] <= size["sb"], (top, size)
+    if K % BKP == 0:
+        assert top["a"] <= size["a"] and top["b"] <= size["b"], (top, size)
     else:
-        over = {k: top[k] - size[k] for k in top}
-        assert max(over["a"], over["b"]) <= 64 and max(over["sa"], over["sb"]) <= 12, over
+        over = {k: top[k] - size[k] for k in ("a", "b")}
+        assert max(over.values()) <= 64, over
+
+
+def test_scale_column_in_the_sgpr_offset_would_read_past():
+    """With the column in the SGPR offset (the earlier form), a half last scale group reads
+    8 bytes past the last row's scales at K = 4352 and 12 at K = 640."""
+    for K, want in ((4352, 8), (640, 12)):
+        top = _fetched_max(256, 256, K, tail=False, scale_col_in_voff=False)
+        assert top["sa"] - _sizes(256, 256, K)["sa"] == want
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -156,8 +175,8 @@ def test_a_wrapping_resource_count_would_admit_the_sentinel():
 
 
 def test_ragged_k_overrun_of_the_kernel_as_built():
-    """K = 384 (a half last buffer): the last row's second half-buffer is admitted by the
-    VGPR check and fetched past the end of the operand; the planned fix does not."""
+    """K = 384 (a half last buffer): the last row's second half-buffer of codes is admitted
+    by the VGPR check and fetched past the end of the operand; the planned fix does not."""
     M, N, K = 300, 260, 384
     top = _fetched_max(M, N, K, tail=False)
     size = _sizes(M, N, K)
