@@ -160,6 +160,7 @@ def _display(cmd):
 
 
 def run(name, out):
+    out = os.path.abspath(out)     # the profiler runs from /tmp: a relative path would land there
     env = dict(os.environ, TMPDIR="/tmp")
     for tag, limit, cmd in _commands(name, out):
         print(f"[profile {name}] {tag}: {_display(cmd)}", flush=True)
