@@ -185,11 +185,9 @@ fp4_status fp4_unpack(const void* packed, int64_t M, int64_t K, void* y, void* s
  *   a_codes [M][K/2], a_scales [M][K/32], b_codes [N][K/2], b_scales [N][K/32],
  *   c [M][N] in ct (FP4_BF16: nearest-even from the fp32 sum; FP4_F32).
  * Shapes: M, N >= 0, K > 0, K % 128 == 0, M*K/2 and N*K/2 below 2^31 bytes.
- * Reads past the operands when K % 256 == 128: the last 256-element step of a row is
- * fetched whole, so at the last row of each operand up to 64 bytes past the end of
- * a_codes / b_codes are read (never written; those products are zeroed).  The caller must
- * leave that much readable memory after each code operand.  For K % 256 == 0 nothing
- * outside the operands is read; scales are never read past their end.
+ * Reads nothing outside the four operands, for every admitted shape: where a load's
+ * 16 bytes would reach past an operand's last row (ragged M/N tiles, a half last
+ * 256-element step of K, a half last scale group), the hardware range check returns zeros.
  */
 fp4_status fp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, fp4_dtype ct,

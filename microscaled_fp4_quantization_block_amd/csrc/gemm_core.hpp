@@ -140,6 +140,7 @@ struct Loader {
   uint32_t scale_off[SW];
   int wave;
   int rot, np;            // starting buffer (even) and buffer count; rot = 0 unless K % 512 == 0
+  int vcol_buf;           // buffer whose code loads carry the column in the VGPR offset (-1: none)
 };
 
 // Buffer that the tile processes at step p: p + rot, wrapped into [0, np).
@@ -156,13 +157,18 @@ __device__ __forceinline__ int rotated(const Loader<NW, FA>& L, int p) {
 // traffic), keeping the control flow straight.
 template <int NW, bool FA>
 __device__ __forceinline__ void issue_codes(const Loader<NW, FA>& L, int p, bool valid, uint8_t* dst) {
-  const int soff = rotated(L, p) * ROWB;
+  const int buf = rotated(L, p);
+  // The half last buffer of a ragged K (K % 256 == 128) carries its column in the VGPR
+  // offset, which the range check covers: its chunks past the operand's last row read
+  // zeros.  Every other buffer keeps the column in the SGPR offset.  Both are wave-uniform.
+  const uint32_t col = (uint32_t)(buf * ROWB);
+  const uint32_t vcol = buf == L.vcol_buf ? col : 0u, scol = col - vcol;
 #pragma unroll
   for (int q = 0; q < Loader<NW, FA>::QW; ++q) {
     uint8_t* blk = dst + (Loader<NW, FA>::QW * L.wave + q) * 1024;
-    const uint32_t off = valid ? L.code_off[q & 1] + (uint32_t)(q & ~1) * L.row_step : kOOB;
-    if constexpr (!FA) dma16(L.rA, blk, off, soff);
-    dma16(L.rB, blk + kCodeBytes, off, soff);
+    const uint32_t off = (valid ? L.code_off[q & 1] + (uint32_t)(q & ~1) * L.row_step : kOOB) + vcol;
+    if constexpr (!FA) dma16(L.rA, blk, off, scol);
+    dma16(L.rB, blk + kCodeBytes, off, scol);
   }
 }
 
@@ -444,6 +450,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
     L.wave = wave;
     L.np = np;
     L.rot = (K % (2 * BKP) == 0) ? (2 * (tile.m0 / BM)) % np : 0;
+    L.vcol_buf = ragged ? np - 1 : -1;
   }
 
   const int wm = (wave / Cfg<NW>::WN) * (32 * TI), wn = (wave % Cfg<NW>::WN) * (32 * TJ);

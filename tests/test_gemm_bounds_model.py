@@ -2,22 +2,23 @@
 
 The kernel loads 16 bytes per lane through raw buffer resources over each tile's rows.  The
 range check of a raw resource covers the VGPR offset only (row and 16-byte chunk here); the
-SGPR offset (the K column) is added to the address after it.  The model mirrors the
-kernel's offset arithmetic (tile rows, the K walk's starting buffer, the XOR chunk swizzle,
-the scale groups, every issue including those past the end of K with their out-of-range
-sentinel), assumes the check admits a dword when VGPR offset + 4 <= num_records, and
-compares the admitted dwords' addresses with the operand's size.
+SGPR offset is added to the address after it.  The model mirrors the kernel's offset
+arithmetic (tile rows, the K walk's starting buffer, the XOR chunk swizzle, the scale
+groups, every issue including those past the end of K with their out-of-range sentinel),
+assumes the check admits a dword when VGPR offset + 4 <= num_records, and compares the
+admitted dwords' addresses with the operand's size.
 
 * The scale loads carry their column in the VGPR offset, so the range check covers it: a
   half last scale group (K % 512 != 0) reads zeros past the operand's last row.
-* K % 256 == 0: every code buffer ends by column K / 2, so nothing leaves the operand.
-* K % 256 == 128 (a half last buffer): the last buffer's chunks past a row's end are
-  admitted and read the next row, and at the operand's last row up to 64 code bytes past
-  its end.  Those bytes only feed products whose scales are zeroed, but they must be
-  mapped: this is an open bound, not a guarantee.
-* The planned fix moves the column offset into the resource base and out of num_records,
-  saturating at zero; the model checks it keeps every fetch inside, and that a count
-  which wraps round instead admits the sentinel offset (2 GiB past the operand).
+* The code loads carry their column in the SGPR offset, except for the half last buffer
+  of a ragged K (K % 256 == 128), whose column goes into the VGPR offset.
+* As built, nothing is fetched outside any operand.  With every code column in the SGPR
+  offset (the earlier form) a ragged K reads up to 64 bytes past the codes' last row; with
+  the scale column there, a half last scale group reads past the scales' last row.  The
+  model checks both, so a change of either placement is caught.
+* A withdrawn form moved the code column into the resource base and subtracted it from
+  the record count; the model shows that a count which wraps round admits the sentinel
+  offset (2 GiB past the operand), and a saturating one does not.
 """
 import numpy as np
 import pytest
@@ -65,53 +66,53 @@ def _issues(np_):
     return codes, scales
 
 
-def _fetched_max(M, N, K, tail, wrap=False, scale_col_in_voff=True):
+def _fetched_max(M, N, K, code_col_in_voff=True, scale_col_in_voff=True, base_shift=False, wrap=False):
     """Largest byte offset + 1 fetched from each operand (A codes, B codes, A scales,
-    B scales) over every tile and issued load, or -1 if none.  `wrap` models a resource
-    count that wraps round instead of saturating when the column exceeds it;
-    `scale_col_in_voff` the scale loads' column in the VGPR offset (as built)."""
+    B scales) over every tile and issued load, or -1 if none.  `code_col_in_voff`: the
+    ragged last code buffer's column in the VGPR offset (as built); `scale_col_in_voff`:
+    the scale loads' column in the VGPR offset (as built).  `base_shift` models a withdrawn
+    form of the code loads: the column moved into the resource base and subtracted from
+    the record count, which saturates at zero, or wraps round with `wrap`."""
     rowbytes, rowscales = K // 2, K // 32
     np_ = (K + BKP - 1) // BKP
+    ragged = K % BKP != 0
     tiles_m, tiles_n = (M + BM - 1) // BM, (N + BN - 1) // BN
     codes_off, scale_off = _lane_offsets(rowbytes, rowscales)
     code_issues, scale_issues = _issues(np_)
     top = {"a": -1, "b": -1, "sa": -1, "sb": -1}
 
-    def admit(key, base, nrec, col, voff, valid, col_in_voff=False):
-        if col_in_voff:
-            voff = (np.asarray(voff, dtype=np.int64) if valid else np.full(64, KOOB, dtype=np.int64)) + col
-            for d in range(4):
-                ok = voff + 4 * d + 4 <= nrec
-                if ok.any():
-                    top[key] = max(top[key], int(base + voff[ok].max() + 4 * d + 4))
-            return
-        if tail:
-            base, soff = base + col, 0
-            nrec = (nrec - col) % (1 << 32) if wrap else max(nrec - col, 0)
-        else:
-            soff = col
+    def admit(key, base, nrec, col, voff, valid, col_in_voff, shift=False):
         voff = np.asarray(voff, dtype=np.int64) if valid else np.full(64, KOOB, dtype=np.int64)
-        for d in range(4):                      # the four dwords of a 16-byte load
+        vcol, scol = (col, 0) if col_in_voff else (0, col)
+        if shift:
+            base, scol = base + col, 0
+            nrec = (nrec - col) % (1 << 32) if wrap else max(nrec - col, 0)
+        voff = voff + vcol
+        assert voff.max() < 1 << 32                 # the 32-bit offset never wraps
+        for d in range(4):                          # the four dwords of a 16-byte load
             ok = voff + 4 * d + 4 <= nrec
             if ok.any():
-                top[key] = max(top[key], int(base + soff + voff[ok].max() + 4 * d + 4))
+                top[key] = max(top[key], int(base + scol + voff[ok].max() + 4 * d + 4))
 
     for tm in range(tiles_m):
         for tn in range(tiles_n):
             m0, n0 = tm * BM, tn * BN
             rows_a, rows_b = min(BM, M - m0), min(BN, N - n0)
             rot = (2 * tm) % np_ if K % (2 * BKP) == 0 else 0
+            vcol_buf = np_ - 1 if ragged and code_col_in_voff and not base_shift else -1
 
             def rotated(q):
                 q += rot
                 return q - np_ if q >= np_ else q
 
             for q, valid in code_issues:
-                col = rotated(q) * ROWB
+                buf = rotated(q)
+                col = buf * ROWB
                 for key, r0, rows in (("a", m0, rows_a), ("b", n0, rows_b)):
                     for wave in range(NW):
                         for i in range(QW):
-                            admit(key, r0 * rowbytes, rows * rowbytes, col, codes_off[wave][i], valid)
+                            admit(key, r0 * rowbytes, rows * rowbytes, col, codes_off[wave][i], valid,
+                                  buf == vcol_buf, base_shift)
             for h, valid in scale_issues:
                 col = (rotated(2 * h) >> 1) * KSCALE_ROW
                 for wave in range(NW):
@@ -119,7 +120,7 @@ def _fetched_max(M, N, K, tail, wrap=False, scale_col_in_voff=True):
                         t = SW * wave + i
                         key, r0, rows = ("sb", n0, rows_b) if t >> 2 else ("sa", m0, rows_a)
                         admit(key, r0 * rowscales, rows * rowscales, col, scale_off[wave][i], valid,
-                              col_in_voff=scale_col_in_voff and not tail)
+                              scale_col_in_voff)
     return top
 
 
@@ -132,53 +133,58 @@ SHAPES = [(1, 1, 128), (64, 96, 256), (300, 260, 384), (256, 512, 1024), (1100, 
           (513, 257, 8192), (130, 70, 640), (200, 300, 1408), (300, 600, 8192)]
 
 
-@pytest.mark.parametrize("M,N,K", SHAPES + [(256, 256, 4352), (300, 260, 4352)])
+@pytest.mark.parametrize("M,N,K", SHAPES + [(256, 256, 4352), (300, 260, 4352), (1, 1, 384), (2, 3, 128)])
 def test_fetches_of_the_kernel_as_built(M, N, K):
-    """The kernel as built: code loads with the column in the SGPR offset, scale loads with
-    it in the VGPR offset."""
-    top = _fetched_max(M, N, K, tail=False)
+    """The kernel as built: every fetch stays inside its operand, and the last row of codes
+    is read whole."""
+    top = _fetched_max(M, N, K)
     size = _sizes(M, N, K)
-    assert top["a"] >= size["a"] and top["b"] >= size["b"]   # the last row is read whole
-    assert top["sa"] <= size["sa"] and top["sb"] <= size["sb"], (top, size)
-    if K % BKP == 0:
-        assert top["a"] <= size["a"] and top["b"] <= size["b"], (top, size)
-    else:
-        over = {k: top[k] - size[k] for k in ("a", "b")}
-        assert max(over.values()) <= 64, over
+    for key in top:
+        assert top[key] <= size[key], (key, top[key], size[key])
+    assert top["a"] == size["a"] and top["b"] == size["b"]
+
+
+@pytest.mark.parametrize("K", [384, 640, 1408, 4224])
+def test_code_column_in_the_sgpr_offset_would_read_past(K):
+    """With every code column in the SGPR offset (the earlier form), a ragged K's last row
+    of codes is followed by 64 fetched bytes past the operand; a K % 256 == 0 is not.
+    (K = 128 has a single buffer, at column 0, where the two forms coincide.)"""
+    for M, N in ((256, 256), (300, 260)):
+        top = _fetched_max(M, N, K, code_col_in_voff=False)
+        size = _sizes(M, N, K)
+        assert top["a"] - size["a"] == 64 and top["b"] - size["b"] == 64
+    top = _fetched_max(256, 256, K + 128, code_col_in_voff=False)
+    assert top["a"] == _sizes(256, 256, K + 128)["a"]
+    top = _fetched_max(256, 256, 128, code_col_in_voff=False)
+    assert top["a"] == _sizes(256, 256, 128)["a"]
 
 
 def test_scale_column_in_the_sgpr_offset_would_read_past():
     """With the column in the SGPR offset (the earlier form), a half last scale group reads
     8 bytes past the last row's scales at K = 4352 and 12 at K = 640."""
     for K, want in ((4352, 8), (640, 12)):
-        top = _fetched_max(256, 256, K, tail=False, scale_col_in_voff=False)
+        top = _fetched_max(256, 256, K, scale_col_in_voff=False)
         assert top["sa"] - _sizes(256, 256, K)["sa"] == want
 
 
-@pytest.mark.parametrize("M,N,K", SHAPES)
-def test_planned_fix_keeps_every_fetch_inside(M, N, K):
-    top = _fetched_max(M, N, K, tail=K % (2 * BKP) != 0)
-    size = _sizes(M, N, K)
-    for key in top:
-        assert top[key] <= size[key], (key, top[key], size[key])
+def test_the_sentinel_stays_out_of_range_with_a_column_added():
+    """An issue past the end of K carries the sentinel offset 2^31; on the ragged last
+    buffer the column is added to it.  The library admits M K / 2 < 2^31 only, so the
+    sum still exceeds every resource's record count, and stays below 2^32."""
+    for K in (128, 384):
+        np_ = (K + BKP - 1) // BKP
+        col = (np_ - 1) * ROWB
+        rows_max = ((1 << 31) - 1) // (K // 2)
+        nrec = min(BM, rows_max) * (K // 2)
+        assert KOOB + col + 16 > nrec and KOOB + col + 16 <= 1 << 32
 
 
 def test_a_wrapping_resource_count_would_admit_the_sentinel():
-    """M = N = 1, K = 128: past the end, rotated() wraps step 0's refill (q = 2) to buffer
-    1, whose column (128) exceeds the operand's 64 bytes.  A count that wraps round to
-    4 GiB admits the out-of-range offset and fetches 2 GiB past the operand; the
-    saturating count admits nothing beyond it."""
-    top = _fetched_max(1, 1, 128, tail=True, wrap=True)
+    """The withdrawn base-shift form at M = N = 1, K = 128: past the end, step 0's refill
+    (q = 2) maps to buffer 1, whose column (128) exceeds the operand's 64 bytes.  A count
+    that wraps round to about 4 GiB admits the out-of-range offset and fetches 2 GiB past
+    the operand (the cause of a GPU fault); a saturating count admits nothing beyond it."""
+    top = _fetched_max(1, 1, 128, base_shift=True, wrap=True)
     assert top["a"] > (1 << 31)
-    top = _fetched_max(1, 1, 128, tail=True)
+    top = _fetched_max(1, 1, 128, base_shift=True)
     assert top["a"] == 64 and top["b"] == 64
-
-
-def test_ragged_k_overrun_of_the_kernel_as_built():
-    """K = 384 (a half last buffer): the last row's second half-buffer of codes is admitted
-    by the VGPR check and fetched past the end of the operand; the planned fix does not."""
-    M, N, K = 300, 260, 384
-    top = _fetched_max(M, N, K, tail=False)
-    size = _sizes(M, N, K)
-    assert top["a"] > size["a"] and top["b"] > size["b"]
-    assert _fetched_max(M, N, K, tail=True)["a"] <= size["a"]

@@ -43,8 +43,9 @@ def test_gemm_random_operands(M, N, K, out):
     if (M, N, K, out) == (1, 1, 128, "f32"):
         pytest.skip("kept off the GPU: this case faulted the GPU twice on two withdrawn forms of the ragged-K "
                     "loads (a resource byte count that wrapped round; a descriptor left in vector registers). "
-                    "The kernel is back to its earlier loads; tests/test_gemm_bounds_model.py and "
-                    "tests/test_kernel_isa.py show both causes on the CPU")
+                    "At this shape the kernel's loads are those of its earlier, tested form; "
+                    "tests/test_gemm_bounds_model.py and tests/test_kernel_isa.py show both causes "
+                    "on the CPU")
     print(f"gemm random M={M} N={N} K={K} {out}", flush=True)
     a, sa = W.random_mxfp4_operand(M, K, seed=M + K)
     b, sb = W.random_mxfp4_operand(N, K, seed=N + 7 * K)
