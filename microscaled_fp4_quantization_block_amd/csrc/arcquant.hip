@@ -46,7 +46,11 @@ constexpr int kPipeK = 8 * 64 * kUnroll;
 constexpr int kPipeTotal = 4096;
 template <bool kGamma>
 constexpr int pipe_waves() { return kGamma ? 16 : 8; }
-constexpr int kMaxGroups = 8;       // load groups of two waves, at most 16 waves
+constexpr int kMaxGroups = 8;       // load groups per workgroup, at most
+// Waves per load group: two in a workgroup of 8 waves, four in one of 16 (gain vector), so
+// that both chains release four groups one after another.
+template <bool kGamma>
+constexpr int group_waves() { return kGamma ? 4 : 2; }
 // Statistics passes end in one atomic maximum per workgroup; atomics on one address
 // serialise, so their grids are capped at kStatsGroups workgroups.
 constexpr int kStatsGroups = 256;
@@ -298,14 +302,33 @@ __device__ __forceinline__ void encode_block_unnormed(const float (&x)[16], floa
 // kBlocks blocks per lane are gathered together (all their LDS reads in flight at once)
 // before any of them is encoded.
 constexpr int kBlocks = 1;
-// Gain of the channel at byte offset `off` of the bf16 row: from gl, gamma in channel order
-// in LDS (its byte offset is 2 off), when kLds, else from global memory.  Where gamma lives
-// is a template parameter: a run-time choice per element compiles to flat loads behind
-// address selects.
-template <bool kLds>
-__device__ __forceinline__ float gain_at(const float* gl, const float* __restrict__ gamma, uint32_t off) {
-  if constexpr (kLds) return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gl) + 2 * off);
-  else return gamma[off >> 1];
+// Gamma staged in LDS for a workgroup (rows of at most kPipeK channels): already
+// permuted to output order, gl holds gamma[perm[c]] for output channel c = BS b + 4 q + e
+// (BS channels per scale block) at float 4 (q (K / BS) + b) + e.  Lane l's gains for
+// block b are then BS / 4 16-byte reads at 16-byte steps across the lanes, with no
+// address arithmetic and no bank conflicts, where a gain looked up by input channel
+// would be one random 4-byte read per element.
+template <int BS>
+__device__ __forceinline__ int gain_slot(int c, int K) {
+  return 4 * (((c % BS) >> 2) * (K / BS) + c / BS) + (c & 3);
+}
+
+template <int BS>
+__device__ __forceinline__ void gains_of_block(const float* gl, int b, int nblk, float (&g)[BS]) {
+  const float4* g4 = reinterpret_cast<const float4*>(gl) + b;
+#pragma unroll
+  for (int q = 0; q < BS / 4; ++q) {
+    const float4 t = g4[q * nblk];
+    g[4 * q] = t.x;
+    g[4 * q + 1] = t.y;
+    g[4 * q + 2] = t.z;
+    g[4 * q + 3] = t.w;
+  }
+}
+
+// Gain of the channel at byte offset `off` of the bf16 row, from global memory (longer rows).
+__device__ __forceinline__ float gain_global(const float* __restrict__ gamma, uint32_t off) {
+  return gamma[off >> 1];
 }
 
 template <bool kGamma, bool kLdsGamma>
@@ -344,10 +367,14 @@ __device__ __forceinline__ void encode_row(const uint16_t* xs, const uint16_t* p
                              pw[j][1].x, pw[j][1].y, pw[j][1].z, pw[j][1].w};
       if constexpr (kGamma) {
         float g[16];
+        if constexpr (kLdsGamma) {
+          gains_of_block<16>(gl, b, nblk, g);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          g[2 * k] = gain_at<kLdsGamma>(gl, gamma, w[k] & 0xFFFFu);
-          g[2 * k + 1] = gain_at<kLdsGamma>(gl, gamma, w[k] >> 16);
+          for (int k = 0; k < 8; ++k) {
+            g[2 * k] = gain_global(gamma, w[k] & 0xFFFFu);
+            g[2 * k + 1] = gain_global(gamma, w[k] >> 16);
+          }
         }
         float z[16];
 #pragma unroll
@@ -399,8 +426,12 @@ __device__ __forceinline__ void encode_row_mx(const uint16_t* xs, const uint16_t
       }
     }
     float g[32];
+    if constexpr (kGamma && kLdsGamma) {
+      gains_of_block<32>(gl, b, nblk, g);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) g[k] = kGamma ? gain_at<kLdsGamma>(gl, gamma, (uint32_t)c[k]) : 1.0f;
+      for (int k = 0; k < 32; ++k) g[k] = kGamma ? gain_global(gamma, (uint32_t)c[k]) : 1.0f;
+    }
     float z[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k)
@@ -436,7 +467,8 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   const int units = K / 8;
   const bool pipelined = units <= 64 * kUnroll;
   // LDS: [K] permutation as byte offsets 2 perm[c]; with a gain vector and short rows,
-  // [K] fp32 gamma in channel order; then one [K] bf16 row per wave.
+  // [K] fp32 gamma permuted to output order (gain_slot); then one [K] bf16 row per wave.
+  constexpr int BS = FMT == fp4impl::FMT_NV ? 16 : 32;
   const bool lds_gamma = kGamma && pipelined;
   uint16_t* ps = smem;
   float* gl = reinterpret_cast<float*>(smem + K);   // used only when lds_gamma
@@ -445,43 +477,55 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   const int64_t stride = (int64_t)gridDim.x * W;
   int64_t r = (int64_t)blockIdx.x * W + wave;
   // An index outside [0, K) (not a permutation: caller error) is clamped, never dereferenced.
-  constexpr int kSt = kPipeK / (64 * pipe_waves<kGamma>());   // staging batch per thread
+  // With a gain vector the table and gamma are staged by the waves past group 0 only:
+  // gamma[perm[c]] is a load that depends on perm[c], and group 0's row loads, issued
+  // first, must not wait behind it.
+  constexpr int kGW = group_waves<kGamma>();
+  constexpr int kLead = kGamma ? kGW : 0;
+  constexpr int kStW = 64 * (pipe_waves<kGamma>() - kLead);
+  constexpr int kSt = (kPipeK + kStW - 1) / kStW;              // staging batch per thread
+  const int nst = (int)blockDim.x - 64 * kLead, st = (int)threadIdx.x - 64 * kLead;
   uint4 raw[kUnroll];
-  if (pipelined && K <= kSt * (int)blockDim.x) {
+  static_assert(pipe_waves<kGamma>() % kGW == 0 && pipe_waves<kGamma>() / kGW <= kMaxGroups, "load groups");
+  if (pipelined && (int)blockDim.x == 64 * pipe_waves<kGamma>() && K <= kSt * nst) {
     // The permutation's loads (L2-resident after the first workgroups) go out first.  The
-    // rows are then requested in groups of two waves: group 0 at once, group g once both
-    // waves of group g - 1 have the first half of their rows in (an LDS counter per
-    // group).  Rows thus land in a steady stream, and each group is encoded while the
-    // next ones arrive: with every row requested at once, all of them would land together
-    // at the end and the encode would start only then.  Group 0 waits for nothing, every
-    // wave counts itself unconditionally, and every group but possibly the last has two
-    // waves, so every wait ends.  A row past M reloads row M - 1, which is then never
-    // used, so every wave takes part.
+    // rows are then requested in groups of kGW waves: group 0 at once, group g once every
+    // wave of group g - 1 has the first half of its row in (an LDS counter per group).
+    // Rows thus land in a steady stream, and each group is encoded while the next ones
+    // arrive: with every row requested at once, all of them would land together at the
+    // end and the encode would start only then.  Group 0 waits for nothing, every wave
+    // counts itself unconditionally, and the workgroup's waves (8 or 16) are a multiple of
+    // kGW, so every group has kGW waves and every wait ends.  A row past M reloads row
+    // M - 1, which is then never used, so every wave takes part.
     uint32_t pv[kSt];
     float gv[kGamma ? kSt : 1];
+    if (st >= 0) {
 #pragma unroll
-    for (int i = 0; i < kSt; ++i) {
-      const int c = min((int)threadIdx.x + i * (int)blockDim.x, K - 1);
-      pv[i] = (uint32_t)perm[c];
-      if constexpr (kGamma) gv[i] = gamma[c];                // coalesced, channel order
+      for (int i = 0; i < kSt; ++i) pv[i] = (uint32_t)perm[min(st + i * nst, K - 1)];
+      if constexpr (kGamma) {
+#pragma unroll
+        for (int i = 0; i < kSt; ++i) gv[i] = gamma[min(pv[i], (uint32_t)(K - 1))];
+      }
     }
     __shared__ uint32_t landed[kMaxGroups];
     const int64_t r0 = r < M ? r : M - 1;
-    const int grp = wave >> 1;
+    const int grp = wave / kGW;
     if (threadIdx.x < kMaxGroups) landed[threadIdx.x] = 0u;
     if (grp == 0) load_units_rsrc(x + r0 * K, units, lane, raw);   // pipelined: one chunk
+    if (st >= 0) {
 #pragma unroll
-    for (int i = 0; i < kSt; ++i) {
-      const int c = threadIdx.x + i * blockDim.x;
-      if (c < K) {
-        ps[c] = (uint16_t)(2 * min(pv[i], (uint32_t)(K - 1)));
-        if constexpr (kGamma) gl[c] = gv[i];
+      for (int i = 0; i < kSt; ++i) {
+        const int c = st + i * nst;
+        if (c < K) {
+          ps[c] = (uint16_t)(2 * min(pv[i], (uint32_t)(K - 1)));
+          if constexpr (kGamma) gl[gain_slot<BS>(c, K)] = gv[i];
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): table and counters written
     __builtin_amdgcn_s_barrier();
     if (grp > 0) {
-      while (__hip_atomic_load(&landed[grp - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 2u)
+      while (__hip_atomic_load(&landed[grp - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)kGW)
         __builtin_amdgcn_s_sleep(1);
       load_units_rsrc(x + r0 * K, units, lane, raw);
     }
@@ -490,8 +534,9 @@ k_arcquant(const uint16_t* __restrict__ x, int64_t M, int K, const float* __rest
   } else {
     if (pipelined && r < M) load_units(x + r * K, 0, units, lane, raw);
     for (int c = threadIdx.x; c < K; c += blockDim.x) {
-      ps[c] = (uint16_t)(2 * min((uint32_t)perm[c], (uint32_t)(K - 1)));
-      if (lds_gamma) gl[c] = gamma[c];
+      const uint32_t pc = min((uint32_t)perm[c], (uint32_t)(K - 1));
+      ps[c] = (uint16_t)(2 * pc);
+      if (lds_gamma) gl[gain_slot<BS>(c, K)] = gamma[pc];
     }
     __syncthreads();
   }

@@ -76,12 +76,14 @@ def test_arcquant_gamma_given_scale_and_random_perm():
     _check_arc(xt, perm, 64, gamma=gamma, eps=1e-5, given=0.0021)
 
 
-def test_arcquant_config_full_size():
-    """bf16 4096 x 4096 N(0,1), 64 outlier channels x30, S = 256 -> K+S = 4352, every row."""
-    print("arcquant 4096x4096 seed 4 S=256", flush=True)
+@pytest.mark.parametrize("gam", [False, True])
+def test_arcquant_config_full_size(gam):
+    """bf16 4096 x 4096 N(0,1), 64 outlier channels x30, S = 256 -> K+S = 4352, every row;
+    with a gain vector (uniform in [0.5, 1.5], seed 7) as the timed gain workload has it."""
+    print(f"arcquant 4096x4096 seed 4 S=256 gamma={gam}", flush=True)
     xt = W.arcquant_input()
     perm = W.calibration_order(xt)
-    n = _check_arc(xt, perm, 256)
+    n = _check_arc(xt, perm, 256, gamma=W.arcquant_gain(4096) if gam else None)
     print(f"  boundary-tolerated code differences: {n}", flush=True)
 
 
