@@ -230,13 +230,14 @@ def cpu_baseline_gemm(a_bf16, w_bf16, rows, rows1=256):
 
 # ----------------------------------------------------------------------------- workloads
 
-def run_w4a4_gemm(args):
+def run_w4a4_gemm(args, name="w4a4_gemm"):
     """The whole hot path per step: Hadamard-32 MXFP4 quantization of one activation batch
     A, then the W4A4 GEMM against the pre-quantized weights.  Steps cycle through
     activation batches totalling >= 1 GiB (A is 128 MiB), so every quantization reads its
     input from HBM rather than from the 256 MB Infinity Cache; the batches are row
-    rotations of the seeded A, the same values in another order."""
-    wl = W.WORKLOADS["w4a4_gemm"]
+    rotations of the seeded A, the same values in another order.  `w4a4_shard` is the
+    same step against one GPU's column shard of the weights (the first N/8 rows)."""
+    wl = W.WORKLOADS[name]
     M, K = wl.shape
     N = wl.extra["N"]
     a_cpu = W.gemm_activations((M, K), wl.seed)
@@ -286,12 +287,14 @@ def run_w4a4_gemm(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1/e8m0 (fp32 accumulate)",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no model weights or datasets)",
-        "config": {"workload": "w4a4_gemm: Hadamard-32 MXFP4 quantization of A bf16 8192x8192 + "
-                               "W4A4 MXFP4 GEMM against rotated MXFP4 weights 28672x8192, bf16 out",
+        "config": {"workload": (f"{name}: Hadamard-32 MXFP4 quantization of A bf16 {M}x{K} + "
+                                f"W4A4 MXFP4 GEMM against rotated MXFP4 weights {N}x{K}, bf16 out"
+                                + (f" (one GPU's column shard of {wl.extra['shards']})" if "shards" in wl.extra else "")),
                    "M": M, "N": N, "K": K, "activation_batches": n_a, "parallelism": "single GPU"},
         "settle": settled,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / FP4_PEAK_TFLOPS, "traffic": _traffic("gemm_w4a4"),
+                     "frac": gemm_tflops / FP4_PEAK_TFLOPS,
+                     "traffic": _traffic("gemm_w4a4" if name == "w4a4_gemm" else f"gemm_{name}"),
                      "kernel": "k_gemm", "kernel_ms": gemm_ms, "flop_per_launch": flops},
         "roofline_quantize": {"bound": "hbm", "achieved": quant_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": quant_gbs / HBM_PEAK_GBS, "traffic": _traffic("quant_mx_h32_a"),
@@ -839,13 +842,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
-                                   "not implemented (run with --gpus 1)"}))
+        print(json.dumps({"error": "the library runs on one GPU only; multi-GPU sharding is not implemented "
+                                   "(--workload w4a4_shard times one GPU's column shard; run with --gpus 1)"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     fp4.lib()                                   # fail loudly if the HIP library is missing
-    runners = {"w4a4_gemm": run_w4a4_gemm, "arcquant_gemm": run_arcquant_gemm, "format_study": run_format_study,
+    runners = {"w4a4_gemm": run_w4a4_gemm, "w4a4_shard": lambda a: run_w4a4_gemm(a, "w4a4_shard"),
+               "arcquant_gemm": run_arcquant_gemm, "format_study": run_format_study,
                "hbm_copy": run_hbm_copy, "hbm_read": run_hbm_read, "mfma_peak": run_mfma_peak,
                "w4a4_fused": run_w4a4_fused}
     out = runners.get(args.workload, run_memory_workload)(args)

@@ -74,6 +74,13 @@ WORKLOADS = {
         "N(0,1), B = Hadamard-rotated MXFP4 weights 28672x8192 from N(0,0.02)",
         (8192, 8192), 5, dict(N=28672, weight_seed=50, weight_std=0.02, tile_seed=500,
                               tiles=64, tile=128)),
+    "w4a4_shard": Workload(
+        "w4a4_shard",
+        "the W4A4 step at one GPU's column shard of eight: Hadamard-32 MXFP4 quantization of "
+        "A bf16 8192x8192 N(0,1), GEMM against the first 3584 of the 28672 rotated MXFP4 "
+        "weight rows (N(0,0.02), the same draw)",
+        (8192, 8192), 5, dict(N=3584, shards=8, weight_seed=50, weight_std=0.02, tile_seed=500,
+                              tiles=64, tile=128)),
 }
 
 

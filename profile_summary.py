@@ -58,6 +58,14 @@ CASES = {
         bench=["--workload", "w4a4_gemm"], steps=20, timed=20, pmc=[SQ_PASS],
         kernels={"k_gemm": ("gemm_w4a4", ["gemm.hip", "gemm_core.hpp"] + DEVICE_HPP, 630194176, 2.0 * M_ * N_ * K_),
                  "k_quant_mx": ("quant_mx_h32_a", ["quant.hip"] + DEVICE_HPP, 169869312, None)}),
+    "w4a4_shard_8192x3584x8192": dict(
+        title="W4A4 step at one GPU's column shard of eight: k_quant_mx<bf16,H32> on one of eight rotating A "
+              "batches (bf16 8192x8192), then k_gemm MXFP4 8192x3584x8192 (the first 3584 of the 28672 weight "
+              "rows), bf16 out",
+        bench=["--workload", "w4a4_shard"], steps=20, timed=20, pmc=[SQ_PASS],
+        kernels={"k_gemm": ("gemm_w4a4_shard", ["gemm.hip", "gemm_core.hpp"] + DEVICE_HPP, 109969408,
+                            2.0 * M_ * 3584 * K_),
+                 "k_quant_mx": (None, [], 169869312, None)}),
     "k_quant_mx_h32_4096x4096": dict(
         title="Hadamard-32 MXFP4 quantization, bf16 4096x4096 with 41 outlier channels x50 (rotating buffers)",
         bench=["--workload", "mxfp4_h32", "--op", "quant"], steps=100, timed=100, pmc=[SQ_PASS],

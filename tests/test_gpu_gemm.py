@@ -120,7 +120,8 @@ def test_w4a4_config_end_to_end():
 
 def test_gemm_config_full_size_sampled_tiles():
     """8192 x 28672 x 8192 (the 70B-class MLP projection shape) on uniform random code
-    bytes (every element value and sign), 64 seeded 128 x 128 tiles."""
+    bytes (every element value and sign), 64 seeded 128 x 128 tiles; and the eight column
+    shards of N / 8 = 3584 weight rows, each against its columns of the whole product."""
     M, N, K = 8192, 28672, 8192
     print("gemm 8192x28672x8192 bf16, 64 tiles", flush=True)
     a, sa = W.random_mxfp4_operand(M, K, seed=5, exp_lo=123, exp_hi=127)
@@ -131,3 +132,12 @@ def test_gemm_config_full_size_sampled_tiles():
         tile = W.values(c[r0:r0 + 128, c0:c0 + 128].cpu())
         ref = gemm.tile(a, sa, b, sb, np.arange(r0, r0 + 128), np.arange(c0, c0 + 128))
         _assert_gemm_close(tile, ref, True)
+    # Column-parallel sharding over eight GPUs (each holds N / 8 = 3584 weight rows): a
+    # tile's K walk and summation order depend on its tile row only, so every shard's
+    # product equals its columns of the whole product bit for bit.
+    ag, sag, bg, sbg = _g(a), _g(sa), _g(b), _g(sb)
+    ns = N // 8
+    for i in range(8):
+        print(f"  column shard {i}: N = {ns}", flush=True)
+        cs = fp4.fp4_gemm(ag, sag, bg[i * ns:(i + 1) * ns], sbg[i * ns:(i + 1) * ns], out_dtype=torch.bfloat16)
+        assert torch.equal(cs.view(torch.int16), c[:, i * ns:(i + 1) * ns].view(torch.int16)), f"shard {i}"

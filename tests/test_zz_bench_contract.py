@@ -42,6 +42,23 @@ def test_default_run_prints_the_contract_line():
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
 
 
+@pytest.mark.gpu
+def test_column_shard_line():
+    """The W4A4 step at one GPU's column shard (N = 28672 / 8 = 3584): one contract line,
+    its GEMM roofline priced on the shard's own FLOP."""
+    print("bench.py --workload w4a4_shard", flush=True)
+    p = _bench("--workload", "w4a4_shard", "--steps", "2", "--warmup", "1", "--settle", "0.2", "--no-cpu",
+               timeout=240)
+    assert p.returncode == 0, p.stderr[-2000:]
+    lines = [l for l in p.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    r = d["roofline"]
+    assert r["bound"] == "mfma" and r["flop_per_launch"] == 2.0 * 8192 * 3584 * 8192
+    assert abs(r["achieved"] - r["flop_per_launch"] / (r["kernel_ms"] * 1e-3) / 1e12) < 1e-6 * r["achieved"]
+    assert d["config"]["N"] == 3584 and "shard" in d["config"]["workload"]
+
+
 MEMORY_WORKLOADS = [("mxfp4_h32", "quant"), ("mxfp4_h32", "dequant"), ("dualscale_pack", "quant"),
                     ("dualscale_pack", "dequant"), ("arcquant", "quant"), ("arcquant_gamma", "quant"),
                     ("arcquant_mx", "quant"), ("nvfp4_roundtrip", "quant")]
