@@ -70,11 +70,14 @@ def test_arcquant_mx_gamma_random_perm():
     _check_arc_mx(xt, perm, 64, gamma=rng.uniform(0.5, 1.5, 256), eps=1e-5)
 
 
-def test_arcquant_mx_config_shape_sampled_rows():
-    print("arcquant mx 4096x4096 seed 4 S=256", flush=True)
+@pytest.mark.parametrize("gam", [False, True])
+def test_arcquant_mx_config_full_size(gam):
+    """The ARCQuant configuration (bf16 4096 x 4096, 64 outlier channels x30, S = 256) in
+    the MXFP4 flavour, every row; with a gain vector (uniform in [0.5, 1.5], seed 7) too."""
+    print(f"arcquant mx 4096x4096 seed 4 S=256 gamma={gam}", flush=True)
     xt = W.arcquant_input()
     perm = W.calibration_order(xt)
-    _, _, n = _check_arc_mx(xt, perm, 256, rows=W.seeded_rows(4096, 48, 41))
+    _, _, n = _check_arc_mx(xt, perm, 256, gamma=W.arcquant_gain(4096) if gam else None)
     print(f"  boundary-tolerated code differences: {n}", flush=True)
 
 
