@@ -38,11 +38,13 @@
 // - Tiles are assigned XCD-aware: consecutive workgroup ids land on different XCDs, so the
 //   id is remapped to give every XCD a contiguous band of tiles, walked in groups of 8
 //   tile-rows, keeping each XCD's L2 working set to a few A and B panels.
-// - When K is a multiple of 512, each tile starts its walk over K at a buffer offset set
-//   by its tile row and wraps around: the tiles that share an A panel stay in step (one
-//   stream of A per panel through L2), while tiles of different rows read different K
-//   columns at any moment, which spreads the load over memory channels.  Only the fp32
-//   summation order changes.
+// - When K is a multiple of 512, tiles in odd tile columns start their walk over K one
+//   scale group (two buffers) in and wrap around: the tiles that share a B panel stay in
+//   step (one stream of B per panel through L2), while neighbouring columns read
+//   different K columns of their A panels at any moment.  Only the fp32 summation order
+//   changes, and it depends on the parity of the tile column alone, so a GEMM over an
+//   even number of 256-column tiles of B gives the same bits as those columns of a wider
+//   product.
 // - bf16 output (N % 8 == 0) leaves through LDS: the accumulators are written as bf16 into
 //   the drained code buffers (16-byte chunks XOR-swizzled by row), then every wave stores
 //   two full 512-byte tile rows per instruction, instead of 8 bytes per lane scattered
@@ -449,7 +451,7 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
     }
     L.wave = wave;
     L.np = np;
-    L.rot = (K % (2 * BKP) == 0) ? (2 * (tile.m0 / BM)) % np : 0;
+    L.rot = (K % (2 * BKP) == 0) ? (2 * ((tile.n0 / BN) & 1)) % np : 0;
     L.vcol_buf = ragged ? np - 1 : -1;
   }
 

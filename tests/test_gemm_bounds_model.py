@@ -3,10 +3,10 @@
 The kernel loads 16 bytes per lane through raw buffer resources over each tile's rows.  The
 range check of a raw resource covers the VGPR offset only (row and 16-byte chunk here); the
 SGPR offset is added to the address after it.  The model mirrors the kernel's offset
-arithmetic (tile rows, the K walk's starting buffer, the XOR chunk swizzle, the scale
-groups, every issue including those past the end of K with their out-of-range sentinel),
-assumes the check admits a dword when VGPR offset + 4 <= num_records, and compares the
-admitted dwords' addresses with the operand's size.
+arithmetic (tile rows, the K walk's starting buffer by tile column parity, the XOR chunk
+swizzle, the scale groups, every issue including those past the end of K with their
+out-of-range sentinel), assumes the check admits a dword when VGPR offset + 4 <=
+num_records, and compares the admitted dwords' addresses with the operand's size.
 
 * The scale loads carry their column in the VGPR offset, so the range check covers it: a
   half last scale group (K % 512 != 0) reads zeros past the operand's last row.
@@ -98,7 +98,7 @@ def _fetched_max(M, N, K, code_col_in_voff=True, scale_col_in_voff=True, base_sh
         for tn in range(tiles_n):
             m0, n0 = tm * BM, tn * BN
             rows_a, rows_b = min(BM, M - m0), min(BN, N - n0)
-            rot = (2 * tm) % np_ if K % (2 * BKP) == 0 else 0
+            rot = (2 * (tn & 1)) % np_ if K % (2 * BKP) == 0 else 0
             vcol_buf = np_ - 1 if ragged and code_col_in_voff and not base_shift else -1
 
             def rotated(q):

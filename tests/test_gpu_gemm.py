@@ -132,9 +132,10 @@ def test_gemm_config_full_size_sampled_tiles():
         tile = W.values(c[r0:r0 + 128, c0:c0 + 128].cpu())
         ref = gemm.tile(a, sa, b, sb, np.arange(r0, r0 + 128), np.arange(c0, c0 + 128))
         _assert_gemm_close(tile, ref, True)
-    # Column-parallel sharding over eight GPUs (each holds N / 8 = 3584 weight rows): a
-    # tile's K walk and summation order depend on its tile row only, so every shard's
-    # product equals its columns of the whole product bit for bit.
+    # Column-parallel sharding over eight GPUs (each holds N / 8 = 3584 weight rows, 14
+    # tile columns): a tile's K walk and summation order depend only on the parity of its
+    # tile column, so every shard's product equals its columns of the whole product bit
+    # for bit.
     ag, sag, bg, sbg = _g(a), _g(sa), _g(b), _g(sb)
     ns = N // 8
     for i in range(8):
