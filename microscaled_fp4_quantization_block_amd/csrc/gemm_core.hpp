@@ -38,10 +38,11 @@
 // - Tiles are assigned XCD-aware: consecutive workgroup ids land on different XCDs, so the
 //   id is remapped to give every XCD a contiguous band of tiles, walked in groups of 8
 //   tile-rows, keeping each XCD's L2 working set to a few A and B panels.
-// - When K is a multiple of 512, tiles in odd tile columns start their walk over K one
-//   scale group (two buffers) in and wrap around: the tiles that share a B panel stay in
-//   step (one stream of B per panel through L2), while neighbouring columns read
-//   different K columns of their A panels at any moment.  Only the fp32 summation order
+// - When K is a multiple of 256, tiles in odd tile columns start their walk over K one
+//   scale group (two buffers) in and wrap around within the whole scale groups (an odd
+//   last buffer, half a group, stays last): the tiles that share a B panel stay in step
+//   (one stream of B per panel through L2), while neighbouring columns read different K
+//   columns of their A panels at any moment.  Only the fp32 summation order
 //   changes, and it depends on the parity of the tile column alone, so a GEMM over an
 //   even number of 256-column tiles of B gives the same bits as those columns of a wider
 //   product.
@@ -141,15 +142,18 @@ struct Loader {
   uint32_t row_step;      // 8 rows in bytes
   uint32_t scale_off[SW];
   int wave;
-  int rot, np;            // starting buffer (even) and buffer count; rot = 0 unless K % 512 == 0
+  int rot, ne, np;        // walk offset (even), buffers it rotates over (even), buffer count
   int vcol_buf;           // buffer whose code loads carry the column in the VGPR offset (-1: none)
 };
 
-// Buffer that the tile processes at step p: p + rot, wrapped into [0, np).
+// Buffer that the tile processes at step p: p + rot wrapped into [0, ne) for the first ne
+// steps, p itself after them.  ne is even and rot is even, so the two steps of a scale
+// group stay one group; an odd last buffer (a half scale group) stays last.
 template <int NW, bool FA>
 __device__ __forceinline__ int rotated(const Loader<NW, FA>& L, int p) {
+  if (p >= L.ne) return p;
   const int q = p + L.rot;
-  return q >= L.np ? q - L.np : q;
+  return q >= L.ne ? q - L.ne : q;
 }
 
 // Issue buffer p (K elements 256 p ..) of both operands into `dst`.  Code instruction g
@@ -176,8 +180,8 @@ __device__ __forceinline__ void issue_codes(const Loader<NW, FA>& L, int p, bool
 
 // Issue scale group h (16 scale bytes per row: K elements 512 h .., counted from the
 // tile's starting buffer) into `dst` ([A rows][16 B] then [B rows][16 B]); instruction t
-// covers rows 64 (t % 4) + l of operand t / 4.  rot is even, so a group never straddles
-// the wrap.  The group's column goes into the VGPR offset, which the descriptor's range
+// covers rows 64 (t % 4) + l of operand t / 4.  rot and ne are even, so a group never
+// straddles the wrap.  The group's column goes into the VGPR offset, which the descriptor's range
 // check covers: when K % 512 != 0 the last group is half a group, and at the operand's
 // last row its second 8 bytes lie past the end; they read as zeros (and are never used).
 template <int NW, bool FA>
@@ -451,7 +455,8 @@ k_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint
     }
     L.wave = wave;
     L.np = np;
-    L.rot = (K % (2 * BKP) == 0) ? (2 * ((tile.n0 / BN) & 1)) % np : 0;
+    L.ne = ragged ? 0 : (np & ~1);                 // a ragged last buffer keeps the walk unrotated
+    L.rot = L.ne >= 4 ? 2 * ((tile.n0 / BN) & 1) : 0;
     L.vcol_buf = ragged ? np - 1 : -1;
   }
 

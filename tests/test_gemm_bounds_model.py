@@ -98,12 +98,15 @@ def _fetched_max(M, N, K, code_col_in_voff=True, scale_col_in_voff=True, base_sh
         for tn in range(tiles_n):
             m0, n0 = tm * BM, tn * BN
             rows_a, rows_b = min(BM, M - m0), min(BN, N - n0)
-            rot = (2 * (tn & 1)) % np_ if K % (2 * BKP) == 0 else 0
+            ne = 0 if ragged else np_ & ~1
+            rot = 2 * (tn & 1) if ne >= 4 else 0
             vcol_buf = np_ - 1 if ragged and code_col_in_voff and not base_shift else -1
 
             def rotated(q):
+                if q >= ne:
+                    return q
                 q += rot
-                return q - np_ if q >= np_ else q
+                return q - ne if q >= ne else q
 
             for q, valid in code_issues:
                 buf = rotated(q)
@@ -130,7 +133,7 @@ def _sizes(M, N, K):
 
 # the GPU test shapes, plus the W4A4 configuration's K with small M, N
 SHAPES = [(1, 1, 128), (64, 96, 256), (300, 260, 384), (256, 512, 1024), (1100, 1300, 1536), (777, 392, 512),
-          (513, 257, 8192), (130, 70, 640), (200, 300, 1408), (300, 600, 8192)]
+          (513, 257, 8192), (130, 70, 640), (200, 300, 1408), (300, 600, 8192), (300, 600, 768), (513, 520, 4352)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES + [(256, 256, 4352), (300, 260, 4352), (1, 1, 384), (2, 3, 128)])
@@ -181,9 +184,10 @@ def test_the_sentinel_stays_out_of_range_with_a_column_added():
 
 def test_a_wrapping_resource_count_would_admit_the_sentinel():
     """The withdrawn base-shift form at M = N = 1, K = 128: past the end, step 0's refill
-    (q = 2) maps to buffer 1, whose column (128) exceeds the operand's 64 bytes.  A count
-    that wraps round to about 4 GiB admits the out-of-range offset and fetches 2 GiB past
-    the operand (the cause of a GPU fault); a saturating count admits nothing beyond it."""
+    (q = 2) has a column beyond the operand's 64 bytes (128 in the walk of that time, which
+    wrapped it to buffer 1; 256 now).  A count that wraps round to about 4 GiB admits the
+    out-of-range offset and fetches 2 GiB past the operand (the cause of a GPU fault); a
+    saturating count admits nothing beyond it."""
     top = _fetched_max(1, 1, 128, base_shift=True, wrap=True)
     assert top["a"] > (1 << 31)
     top = _fetched_max(1, 1, 128, base_shift=True)

@@ -37,7 +37,8 @@ def _assert_gemm_close(c, ref, bf16):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (64, 96, 256), (300, 260, 384), (256, 512, 1024), (1100, 1300, 1536),
-                                   (777, 392, 512), (513, 257, 8192), (130, 70, 640), (200, 300, 1408)])
+                                   (777, 392, 512), (513, 257, 8192), (130, 70, 640), (200, 300, 1408),
+                                   (300, 600, 768), (513, 520, 4352)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_random_operands(M, N, K, out):
     if (M, N, K, out) == (1, 1, 128, "f32"):
