@@ -22,9 +22,10 @@
 //      Lanes whose block lies in the first S channels also encode the residual
 //      z - V s_b s_t (one fma: a single rounding of the exact difference).
 // Rows of up to 4096 channels are one load per wave.  A workgroup requests its rows in
-// groups of two waves, each group released once the previous one has half its rows in,
-// so rows land in a steady stream and the early ones are encoded under the later ones'
-// traffic (see k_arcquant).
+// groups of two waves (four with a gain vector), each group released once the previous
+// one has half its rows in, so rows land in a steady stream and the early ones are
+// encoded under the later ones' traffic (see k_arcquant).  With a gain vector, gamma is
+// staged in LDS once per workgroup, already permuted to output order (see gain_slot).
 // The dynamic tensor scale needs max|z| over the tensor first.  The maximum does not
 // depend on channel order, so the statistics pass streams rows without the gather, with
 // the same per-element arithmetic as the quantizing pass.

@@ -181,9 +181,10 @@ __device__ __forceinline__ void issue_codes(const Loader<NW, FA>& L, int p, bool
 // Issue scale group h (16 scale bytes per row: K elements 512 h .., counted from the
 // tile's starting buffer) into `dst` ([A rows][16 B] then [B rows][16 B]); instruction t
 // covers rows 64 (t % 4) + l of operand t / 4.  rot and ne are even, so a group never
-// straddles the wrap.  The group's column goes into the VGPR offset, which the descriptor's range
-// check covers: when K % 512 != 0 the last group is half a group, and at the operand's
-// last row its second 8 bytes lie past the end; they read as zeros (and are never used).
+// straddles the wrap.  The group's column goes into the VGPR offset, which the
+// descriptor's range check covers: when K % 512 != 0 the last group is half a group, and
+// at the operand's last row its second 8 bytes lie past the end; they read as zeros (and
+// are never used).
 template <int NW, bool FA>
 __device__ __forceinline__ void issue_scales(const Loader<NW, FA>& L, int h, bool valid, uint8_t* dst) {
   const uint32_t col = (uint32_t)((rotated(L, 2 * h) >> 1) * kScaleRow);

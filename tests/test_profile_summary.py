@@ -79,5 +79,28 @@ def test_summary_arithmetic(fake):
     entry = json.loads(traffic.read_text())["fake_key"]
     assert entry["bytes"] == 500 * 1024 * 2 + 100 * 1024
     assert entry["sources"] == ["k.hip"]
-    assert entry["source_sha"] == hashlib.sha256(b"kernel source\n").hexdigest()[:16]
+    assert entry["source_sha"] == hashlib.sha256(b"kernel source\0").hexdigest()[:16]
     assert entry["profile"] == "profiles/fake.txt"
+
+
+def test_code_text_drops_comments_and_layout_only():
+    src = ('int a = 1; // note "x"\n/* block\n comment */ const char* s = "a // kept";\n'
+           "char c = '/';  int   b;\n")
+    assert P.code_text(src) == 'int a = 1; const char* s = "a // kept"; char c = \'/\'; int b;'
+    assert P.code_text('x = "q \\" // in the string"; // gone\n') == 'x = "q \\" // in the string";'
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """A traffic entry stays valid across comment and layout edits of its kernel sources and
+    is voided by a change of code; bench.py and profile_summary.py hash alike."""
+    import bench
+    k = tmp_path / "k.hip"
+    monkeypatch.setattr(P, "CSRC", str(tmp_path))
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    k.write_text("__global__ void f(int* p) { p[0] = 1; }\n")
+    h0 = P.source_sha(["k.hip"])
+    assert bench.source_sha(["k.hip"]) == h0
+    k.write_text("// what f does\n__global__ void f(int* p) {\n  p[0] = 1;  /* one */\n}\n")
+    assert P.source_sha(["k.hip"]) == h0
+    k.write_text("__global__ void f(int* p) { p[0] = 2; }\n")
+    assert P.source_sha(["k.hip"]) != h0
