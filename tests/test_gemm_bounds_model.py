@@ -133,7 +133,8 @@ def _sizes(M, N, K):
 
 # the GPU test shapes, plus the W4A4 configuration's K with small M, N
 SHAPES = [(1, 1, 128), (64, 96, 256), (300, 260, 384), (256, 512, 1024), (1100, 1300, 1536), (777, 392, 512),
-          (513, 257, 8192), (130, 70, 640), (200, 300, 1408), (300, 600, 8192), (300, 600, 768), (513, 520, 4352)]
+          (513, 257, 8192), (130, 70, 640), (200, 300, 1408), (300, 600, 8192), (300, 600, 768), (513, 520, 4352),
+          (300, 1100, 1280)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES + [(256, 256, 4352), (300, 260, 4352), (1, 1, 384), (2, 3, 128)])

@@ -119,6 +119,25 @@ def test_w4a4_config_end_to_end():
         _assert_gemm_close(tile, ref, True)
 
 
+@pytest.mark.parametrize("K", [1280, 4352, 8192, 1408])
+def test_gemm_column_slices_keep_the_bits(K):
+    """A product over the weight rows from an even 256-column tile onwards equals those
+    columns of the whole product bit for bit: the K walk starts by the parity of the tile
+    column (for K a multiple of 256, rotating within whole scale groups; a ragged K does
+    not rotate).  N = 1100 makes the last tile column ragged."""
+    M, N = 300, 1100
+    print(f"gemm column slices M={M} N={N} K={K}", flush=True)
+    a, sa = W.random_mxfp4_operand(M, K, seed=K + 1)
+    b, sb = W.random_mxfp4_operand(N, K, seed=K + 2)
+    ag, sag, bg, sbg = _g(a), _g(sa), _g(b), _g(sb)
+    c = fp4.fp4_gemm(ag, sag, bg, sbg, out_dtype=torch.float32)
+    for n0 in (512, 1024):
+        cs = fp4.fp4_gemm(ag, sag, bg[n0:], sbg[n0:], out_dtype=torch.float32)
+        assert torch.equal(cs.view(torch.int32), c[:, n0:].contiguous().view(torch.int32)), n0
+    ref = gemm.tile(a, sa, b, sb, np.arange(0, 64), np.arange(N - 100, N))
+    _assert_gemm_close(W.values(c[:64, N - 100:].cpu()), ref, False)
+
+
 def test_gemm_config_full_size_sampled_tiles():
     """8192 x 28672 x 8192 (the 70B-class MLP projection shape) on uniform random code
     bytes (every element value and sign), 64 seeded 128 x 128 tiles; and the eight column
