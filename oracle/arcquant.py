@@ -41,12 +41,13 @@ def rmsnorm(x, gamma=None, eps=1e-6):
 
 
 def quantize(x, perm, S, gamma=None, eps=1e-6, tensor_scale_value=None,
-             primary_scales=None, primary_codes=None, residual_scales=None):
+             primary_scales=None, primary_codes=None, residual_scales=None, z=None):
     """Fused ARCQuant activation quantization of [M, K] into the [K | S] layout.
 
     The optional overrides replace a decision by a given one (E4M3 codes for the
     scales, unpacked codes for the primary elements), so that each later decision can
-    be checked against the oracle given the earlier ones.
+    be checked against the oracle given the earlier ones; `z` replaces the normalized,
+    reordered values [M, K] (the steps from the tensor scale on are unchanged).
 
     Returns `packed` [M, (K+S)/2], `scales` [M, (K+S)/16] (E4M3), `tensor_scale`, the
     normalized-and-reordered values `z`, and per stage the codes and decision
@@ -57,7 +58,7 @@ def quantize(x, perm, S, gamma=None, eps=1e-6, tensor_scale_value=None,
     perm = np.asarray(perm, dtype=np.int64)
     assert sorted(perm.tolist()) == list(range(K)), "perm must be a permutation of 0..K-1"
     assert S % BLOCK == 0 and 0 <= S <= K and K % BLOCK == 0
-    z = rmsnorm(x, gamma, eps)[:, perm]
+    z = rmsnorm(x, gamma, eps)[:, perm] if z is None else np.asarray(z, dtype=np.float64).reshape(M, K)
     s_t = nvfp4.tensor_scale(z) if tensor_scale_value is None else np.float32(tensor_scale_value)
     pc, psb, parg, pq = nvfp4.quantize_blocks(z, s_t, primary_scales)
     if primary_codes is not None:
@@ -87,7 +88,7 @@ def dequantize(packed, scales, s_t, K, S):
 
 
 def quantize_mx(x, perm, S, gamma=None, eps=1e-6, primary_scales=None, primary_codes=None,
-                residual_scales=None):
+                residual_scales=None, z=None):
     """MXFP4 flavour of the fused activation quantization, [K | S] layout.
 
     The ARCQuant summary (Résultats Expérimentaux, Généralisabilité) reports that the
@@ -97,7 +98,8 @@ def quantize_mx(x, perm, S, gamma=None, eps=1e-6, primary_scales=None, primary_c
     of the primary quantization on the first S channels, quantized with its own E8M0
     block scales.  There is no tensor scale.  S and K are multiples of 32.
 
-    Overrides replace decisions by given ones, as in quantize().  Returns `packed`
+    Overrides replace decisions (and `z` the normalized, reordered values) by given ones,
+    as in quantize().  Returns `packed`
     [M, (K+S)/2], `scales` [M, (K+S)/32] (E8M0), `z`, `residual_value`, and `primary` /
     `residual` dicts with codes, scales, block maxima `amax` and element arguments.
     """
@@ -107,7 +109,7 @@ def quantize_mx(x, perm, S, gamma=None, eps=1e-6, primary_scales=None, primary_c
     assert sorted(perm.tolist()) == list(range(K)), "perm must be a permutation of 0..K-1"
     B = mxfp4.BLOCK
     assert S % B == 0 and 0 <= S <= K and K % B == 0
-    z = rmsnorm(x, gamma, eps)[:, perm]
+    z = rmsnorm(x, gamma, eps)[:, perm] if z is None else np.asarray(z, dtype=np.float64).reshape(M, K)
     p = mxfp4.quantize(z, 0, primary_scales)
     pc = p["codes"] if primary_codes is None else np.asarray(primary_codes, dtype=np.uint8).reshape(M, K)
     xhat = mxfp4.dequantize_exact(pc, p["scales"])

@@ -44,13 +44,18 @@ def _check_arc(xt, perm, S, gamma=None, eps=1e-6, rows=None, given=None):
     c1 = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst, primary_scales=gs[:, :nb])
     n = P.check_e2m1_codes(gc[:, :K], c1["primary"]["codes"], c1["primary"]["elem_arg"], c1["z"], 16,
                            what="primary codes")
+    # The residual z - V s_b s_t is a difference: z's fp32 error (held to 1e-5 of the row
+    # maximum above) carries over whole, which can exceed 1e-5 of the residual's own
+    # argument where a residual block is small against the row.  Its decisions are
+    # therefore checked given the GPU's own z as well as its primary codes and scales.
+    zg = _np(dbg)[rows]
     c2 = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst, primary_scales=gs[:, :nb],
-                           primary_codes=gc[:, :K])
+                           primary_codes=gc[:, :K], z=zg)
     if S:
         P.check_e4m3_scales(gs[:, nb:], c2["residual"]["scales"], c2["residual"]["scale_arg"],
                             what="residual scales")
         c3 = arcquant.quantize(xr, perm, S, gam, eps, tensor_scale_value=gst, primary_scales=gs[:, :nb],
-                               primary_codes=gc[:, :K], residual_scales=gs[:, nb:])
+                               primary_codes=gc[:, :K], residual_scales=gs[:, nb:], z=zg)
         n += P.check_e2m1_codes(gc[:, K:], c3["residual"]["codes"], c3["residual"]["elem_arg"],
                                 c3["residual_value"], 16, what="residual codes")
     return n

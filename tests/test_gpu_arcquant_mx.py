@@ -37,10 +37,12 @@ def _check_arc_mx(xt, perm, S, gamma=None, eps=1e-6, rows=None):
     n = P.check_e2m1_codes(gc[:, :K], c1["primary"]["codes"], c1["primary"]["elem_arg"], c1["z"], 32,
                            what="primary codes")
     if S:
-        c2 = arcquant.quantize_mx(xr, perm, S, gam, eps, primary_scales=gs[:, :nb], primary_codes=gc[:, :K])
+        # residual decisions given the GPU's own z (see the NVFP4 check)
+        zg = _np(dbg)[rows]
+        c2 = arcquant.quantize_mx(xr, perm, S, gam, eps, primary_scales=gs[:, :nb], primary_codes=gc[:, :K], z=zg)
         P.check_e8m0_scales(gs[:, nb:], c2["residual"]["scales"], c2["residual"]["amax"], what="residual scales")
         c3 = arcquant.quantize_mx(xr, perm, S, gam, eps, primary_scales=gs[:, :nb], primary_codes=gc[:, :K],
-                                  residual_scales=gs[:, nb:])
+                                  residual_scales=gs[:, nb:], z=zg)
         n += P.check_e2m1_codes(gc[:, K:], c3["residual"]["codes"], c3["residual"]["elem_arg"],
                                 c3["residual_value"], 32, what="residual codes")
     return codes, scales, n

@@ -309,6 +309,24 @@ def test_arcquant_zero_residual_channels_and_identity_perm():
     assert np.array_equal(r0["codes"], n["codes"]) and np.array_equal(r0["scales"], n["scales"])
 
 
+def test_arcquant_z_override_is_the_same_steps():
+    """Given its own normalized, reordered values, the oracle reproduces its default result
+    exactly (both flavours); given other values, those are what the residual is taken
+    from (the parity checks condition the residual on the GPU's z this way)."""
+    x, perm, S = _arc_case(seed=46, M=6, K=256, S=64)
+    g = np.random.default_rng(47).uniform(-1.5, 1.5, 256)
+    z = arcquant.rmsnorm(x, g, 1e-6)[:, perm]
+    for fn in (arcquant.quantize, arcquant.quantize_mx):
+        a = fn(x, perm, S, g, 1e-6)
+        b = fn(x, perm, S, g, 1e-6, z=z)
+        for key in ("codes", "scales", "z", "residual_value"):
+            assert np.array_equal(a[key], b[key]), (fn.__name__, key)
+        zp = z * (1 + 2.0 ** -20)
+        c = fn(x, perm, S, g, 1e-6, primary_scales=a["primary"]["scales"], primary_codes=a["primary"]["codes"], z=zp)
+        assert np.array_equal(c["z"], zp)
+        assert not np.array_equal(c["residual_value"], a["residual_value"])
+
+
 def test_arcquant_mx_against_exact_bruteforce():
     """MXFP4 flavour: E8M0 per 32 on z, residual against the exact primary value."""
     x, perm, S = _arc_case(seed=46, M=3, K=128, S=64)
