@@ -10,7 +10,8 @@ import torch
 
 import microscaled_fp4_quantization_block_amd as fp4
 from microscaled_fp4_quantization_block_amd import workloads as W
-from oracle import gemm
+from oracle import formats as F, gemm, nvfp4
+from tests import parity as P
 from tests.test_gpu_arcquant import _check_arc
 from tests.test_gpu_arcquant_mx import _check_arc_mx
 from tests.test_gpu_gemm import _assert_gemm_close, _g
@@ -18,6 +19,7 @@ from tests.test_gpu_pack import _check_pack
 from tests.test_gpu_quantize import _check_mx_rotated, _nvfp4_exact_case
 
 pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
 
 _rng = np.random.default_rng(20261203)
 
@@ -27,24 +29,31 @@ def _rows():
 
 
 # (M, K, input dtype) for the exact NVFP4 round trip; K a multiple of 32
-NV_EXACT = [(_rows(), 32 * int(_rng.integers(1, 33)), str(_rng.choice(["bf16", "f32"]))) for _ in range(8)]
+NV_EXACT = [(_rows(), 32 * int(_rng.integers(1, 33)), str(_rng.choice(["bf16", "f32"]))) for _ in range(16)]
 # (M, K, h) for rotated MXFP4; K a multiple of max(32, h)
 MX_ROT = []
-for _ in range(9):
+for _ in range(18):
     h = int(_rng.choice([16, 32, 128]))
     MX_ROT.append((_rows(), max(32, h) * int(_rng.integers(1, 17 if h == 128 else 33)), h))
+# (M, K, h) for rotated NVFP4 with the dynamic tensor scale
+NV_ROT = []
+for _ in range(12):
+    h = int(_rng.choice([16, 32, 128]))
+    NV_ROT.append((_rows(), max(32, h) * int(_rng.integers(1, 17 if h == 128 else 33)), h))
 # (M, K) for the dual-scale pack; K a multiple of 128
-PACK = [(_rows(), 128 * int(_rng.integers(1, 17))) for _ in range(6)]
-# (M, K, S, gamma) for ARCQuant NVFP4 (K a multiple of 16) and MXFP4 (of 32); two rows past
+PACK = [(_rows(), 128 * int(_rng.integers(1, 17))) for _ in range(12)]
+# (M, K, S, gamma) for ARCQuant NVFP4 (K a multiple of 16) and MXFP4 (of 32); two shapes each with rows past
 # one 4096-channel chunk each
-ARC_NV = [(_rows(), 16 * int(_rng.integers(1, 257)), None, bool(_rng.integers(0, 2))) for _ in range(6)]
-ARC_NV += [(int(_rng.integers(1, 40)), 4096 + 16 * int(_rng.integers(1, 257)), None, bool(_rng.integers(0, 2)))]
-ARC_MX = [(_rows(), 32 * int(_rng.integers(1, 129)), None, bool(_rng.integers(0, 2))) for _ in range(6)]
-ARC_MX += [(int(_rng.integers(1, 40)), 4096 + 32 * int(_rng.integers(1, 129)), None, bool(_rng.integers(0, 2)))]
+ARC_NV = [(_rows(), 16 * int(_rng.integers(1, 257)), None, bool(_rng.integers(0, 2))) for _ in range(12)]
+ARC_NV += [(int(_rng.integers(1, 40)), 4096 + 16 * int(_rng.integers(1, 257)), None, bool(_rng.integers(0, 2)))
+           for _ in range(2)]
+ARC_MX = [(_rows(), 32 * int(_rng.integers(1, 129)), None, bool(_rng.integers(0, 2))) for _ in range(12)]
+ARC_MX += [(int(_rng.integers(1, 40)), 4096 + 32 * int(_rng.integers(1, 129)), None, bool(_rng.integers(0, 2)))
+           for _ in range(2)]
 ARC_NV = [(m, k, 16 * int(_rng.integers(0, k // 16 + 1)), g) for m, k, _, g in ARC_NV]
 ARC_MX = [(m, k, 32 * int(_rng.integers(0, k // 32 + 1)), g) for m, k, _, g in ARC_MX]
 # (M, N, K) for the GEMM; K a multiple of 128 from 256 up
-GEMM = [(int(_rng.integers(1, 700)), int(_rng.integers(1, 700)), 128 * int(_rng.integers(2, 25))) for _ in range(8)]
+GEMM = [(int(_rng.integers(1, 700)), int(_rng.integers(1, 700)), 128 * int(_rng.integers(2, 25))) for _ in range(14)]
 
 
 def _input(M, K, seed, dtype="bf16"):
@@ -66,6 +75,24 @@ def test_sweep_nvfp4_roundtrip_exact(M, K, dt):
 def test_sweep_mxfp4_rotated(M, K, h):
     print(f"sweep mxfp4 H{h} M={M} K={K}", flush=True)
     _check_mx_rotated(_input(M, K, M * 11 + K + h), h)
+
+
+@pytest.mark.parametrize("M,K,h", NV_ROT)
+def test_sweep_nvfp4_rotated_dynamic_scale(M, K, h):
+    print(f"sweep nvfp4 H{h} M={M} K={K}", flush=True)
+    xt = _input(M, K, M * 23 + K + h)
+    dbg = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    codes, scales, ts = fp4.fp4_quantize(xt.to(DEV), "nvfp4", h, dbg_rotated=dbg)
+    xv = W.values(xt)
+    ref = nvfp4.quantize(xv, hadamard=h)
+    d = dbg.cpu().numpy()
+    P.assert_values_close(d, ref["y"], h, what="rotated values")
+    gst = ts.cpu().numpy()[0]
+    assert gst == np.float32(np.max(np.abs(d))) / np.float32(2688.0)    # of the kernel's own values
+    c1 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst)
+    P.check_e4m3_scales(scales.cpu().numpy(), c1["scales"], c1["scale_arg"])
+    c2 = nvfp4.quantize(xv, hadamard=h, tensor_scale_value=gst, block_scales=scales.cpu().numpy())
+    P.check_e2m1_codes(F.unpack_nibbles(codes.cpu().numpy()), c2["codes"], c2["elem_arg"], c2["y"], 16)
 
 
 @pytest.mark.parametrize("M,K", PACK)
