@@ -188,6 +188,9 @@ fp4_status fp4_unpack(const void* packed, int64_t M, int64_t K, void* y, void* s
  * Reads nothing outside the four operands, for every admitted shape: where a load's
  * 16 bytes would reach past an operand's last row (ragged M/N tiles, a half last
  * 256-element step of K, a half last scale group), the hardware range check returns zeros.
+ * Deterministic: the fp32 summation order of C[m][n] depends only on K and on the parity
+ * of n / 256, so a product over the rows of B from a multiple of 512 onward (a column
+ * shard) gives the same bits as those columns of the wider product.
  */
 fp4_status fp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, fp4_dtype ct,
