@@ -104,3 +104,34 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert P.source_sha(["k.hip"]) == h0
     k.write_text("__global__ void f(int* p) { p[0] = 2; }\n")
     assert P.source_sha(["k.hip"]) != h0
+
+
+def test_bench_traffic_entry_follows_its_sources(tmp_path, monkeypatch):
+    """bench.py reports an entry's calibrated bytes while the kernel code matches the hash
+    it was measured with, keeps them across a comment edit, and reports None after a code
+    change or when the entry is missing."""
+    import bench
+    (tmp_path / "csrc").mkdir()
+    k = tmp_path / "csrc" / "k.hip"
+    k.write_text("__global__ void f(int* p) { p[0] = 1; }\n")
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path / "csrc"))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    (tmp_path / "traffic.json").write_text(json.dumps(
+        {"k": {"bytes": 1234, "sources": ["k.hip"], "source_sha": bench.source_sha(["k.hip"])}}))
+    assert bench._traffic("k") == 1234
+    k.write_text("// f stores one\n__global__ void f(int* p) { p[0] = 1; }\n")
+    assert bench._traffic("k") == 1234
+    k.write_text("__global__ void f(int* p) { p[0] = 2; }\n")
+    assert bench._traffic("k") is None
+    assert bench._traffic("missing") is None
+
+
+def test_source_hash_of_every_kernel_source_list():
+    """The hash reads every source list the profiles name (UTF-8 comments included)."""
+    import bench
+    entries = json.load(open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                          "profiles", "traffic.json")))
+    for key, e in entries.items():
+        if isinstance(e, dict) and "sources" in e:
+            h = bench.source_sha(e["sources"])
+            assert len(h) == 16 and h == P.source_sha(e["sources"]), key
