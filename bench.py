@@ -678,11 +678,12 @@ def _memory_case(name, op):
     raise SystemExit(f"unknown workload {name}")
 
 
-def _memory_pass(args, make, launch, nbytes):
+def _memory_pass(args, make, launch, nbytes, reps=5, samples=None):
     """One measurement: fresh rotating buffer sets, the settle phase, warmup launches, then
     `steps` launches captured into one HIP graph; after an untimed replay (which uploads the
-    graph) one replay is timed with a HIP event pair on the replay stream.  Returns
-    (mean ms per launch, wall seconds of the timed replay, settle record)."""
+    graph) `reps` replays are timed, each with its own HIP event pair on the replay stream.
+    Returns (median over the replays of the mean ms per launch, median wall seconds of a
+    replay, settle record); `samples`, when given, receives every replay's ms per launch."""
     sets = _rotating(make, nbytes)
     i = [0]
 
@@ -701,20 +702,25 @@ def _memory_pass(args, make, launch, nbytes):
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    kms, walls = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        kms.append(e0.elapsed_time(e1) / args.steps)
     del g, sets
-    return e0.elapsed_time(e1) / args.steps, wall, settled
+    if samples is not None:
+        samples.extend(kms)
+    return float(np.median(kms)), float(np.median(walls)), settled
 
 
 def run_memory_workload(args):
     """K launches over rotating buffer sets, captured once into a HIP graph so that the
-    host's launch cost does not pace these short kernels; the timed region is one replay
-    bracketed by one HIP event pair on the replay stream.
+    host's launch cost does not pace these short kernels; five replays are timed, each
+    bracketed by one HIP event pair on the replay stream, and the median is reported.
 
     The whole measurement runs twice and the second is reported: the first pass of a
     process over freshly allocated buffers can be slower (the dual-scale unpack measured
@@ -725,7 +731,8 @@ def run_memory_workload(args):
     wl = W.WORKLOADS[name]
     make, launch, nbytes, kernel, cpu = _memory_case(name, op)
     first_kms, _, _ = _memory_pass(args, make, launch, nbytes)
-    kms, wall, settled = _memory_pass(args, make, launch, nbytes)
+    replays = []
+    kms, wall, settled = _memory_pass(args, make, launch, nbytes, samples=replays)
     gbs = nbytes / (kms * 1e-3) / 1e9
     out = {"metric": METRIC, "value": nbytes * args.steps / wall / 1e9, "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
@@ -736,10 +743,10 @@ def run_memory_workload(args):
            "settle": settled,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(f"{name}_{op}"), "kernel": kernel,
-                        "kernel_ms": kms, "first_pass_kernel_ms": first_kms, "bytes_per_launch": nbytes,
-                        "buffer_sets": len(_rotating_count(nbytes)),
-                        "timing": "one HIP event pair around a graph replay of `steps` launches, "
-                                  "second of two passes"}}
+                        "kernel_ms": kms, "kernel_ms_replays": replays, "first_pass_kernel_ms": first_kms,
+                        "bytes_per_launch": nbytes, "buffer_sets": len(_rotating_count(nbytes)),
+                        "timing": "median of five graph replays of `steps` launches, each between one "
+                                  "HIP event pair; second of two passes"}}
     if not args.no_cpu:
         oname, chunk, rows, what = cpu
         out["cpu_baseline"] = cpu_baseline_rows(oname, chunk, rows, nbytes / wl.shape[0], what)

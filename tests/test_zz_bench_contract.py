@@ -80,5 +80,7 @@ def test_memory_workload_lines(workload, op):
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["achieved"] > 0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
     assert r["kernel_ms"] > 0 and r["first_pass_kernel_ms"] > 0 and r["bytes_per_launch"] > 0
+    reps = sorted(r["kernel_ms_replays"])
+    assert len(reps) == 5 and reps[2] == r["kernel_ms"]              # the median of five replays
     assert abs(r["achieved"] - r["bytes_per_launch"] / (r["kernel_ms"] * 1e-3) / 1e9) < 1e-6 * r["achieved"]
     assert workload in d["config"]["workload"]
