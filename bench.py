@@ -171,6 +171,10 @@ def _oracle_op(name, data):
         mxfp4.quantize(data[0], hadamard=32)
     elif name == "mxfp4_h32_dequant":
         mxfp4.dequantize(data[0], data[1], inverse_hadamard=32)
+    elif name == "nvfp4_h16_quant":
+        nvfp4.quantize(data[0], hadamard=16, tensor_scale_value=data[1])
+    elif name == "nvfp4_h16_dequant":
+        nvfp4.dequantize(data[0], data[1], data[2], inverse_hadamard=16)
     elif name == "dualscale_pack_quant":
         dualscale.pack_values(data[0])
     elif name == "dualscale_pack_dequant":
@@ -592,6 +596,33 @@ def _memory_case(name, op):
         cpu = ("mxfp4_h32_dequant", lambda lo, hi: (cn[lo:hi], sn[lo:hi]), M,
                "oracle mxfp4.dequantize(inverse_hadamard=32)")
         return make, launch, nbytes, "k_dequant<MX,32,bf16> (inverse H32)", cpu
+    if name == "nvfp4_h16":
+        x_cpu = W.mxfp4_h32_input(wl.shape, wl.seed)
+        nbytes = M * K * 2 + M * K // 2 + M * K // 16 + 4
+        xv = W.values(x_cpu)
+        ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+        codes, scales, _ = fp4.fp4_quantize(x_cpu.to(DEV), "nvfp4", 16, tensor_scale=ts)   # calibrate once
+        st = np.float32(ts.cpu().numpy()[0])
+        if op == "quant":
+            def make():
+                return (x_cpu.to(DEV), torch.empty((M, K // 2), dtype=torch.uint8, device=DEV),
+                        torch.empty((M, K // 16), dtype=torch.uint8, device=DEV))
+
+            def launch(s):
+                fp4.fp4_quantize(s[0], "nvfp4", 16, codes=s[1], scales=s[2], tensor_scale=ts, mode="given")
+            cpu = ("nvfp4_h16_quant", lambda lo, hi: (xv[lo:hi], st), M,
+                   "oracle nvfp4.quantize(hadamard=16) with the calibrated tensor scale")
+            return make, launch, nbytes, "k_quant_nv<bf16,16> (static tensor scale)", cpu
+        cn, sn = codes.cpu().numpy(), scales.cpu().numpy()
+
+        def make():
+            return (codes.clone(), scales.clone(), torch.empty((M, K), dtype=torch.bfloat16, device=DEV))
+
+        def launch(s):
+            fp4.fp4_dequantize(s[0], s[1], ts, "nvfp4", 16, y=s[2])
+        cpu = ("nvfp4_h16_dequant", lambda lo, hi: (cn[lo:hi], sn[lo:hi], st), M,
+               "oracle nvfp4.dequantize(inverse_hadamard=16)")
+        return make, launch, nbytes, "k_dequant<NV,16,bf16> (inverse H16)", cpu
     if name == "dualscale_pack":
         x_cpu = W.student_t_input(wl.shape, wl.seed)
         nbytes = M * K * 2 + M * K // 2 + M * K // 16 + 4 * M * K // 128

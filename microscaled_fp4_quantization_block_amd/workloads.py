@@ -40,6 +40,12 @@ WORKLOADS = {
         "MXFP4 quantize with block Hadamard 32: bf16 4096x4096 N(0,1), 41 outlier "
         "channels x50, E8M0 per 32, packed output + dequant",
         (4096, 4096), 2, dict(outliers=41, outlier_gain=50.0)),
+    "nvfp4_h16": Workload(
+        "nvfp4_h16",
+        "NVFP4 quantize with block Hadamard 16 and a calibrated (static) FP32 tensor scale: the "
+        "MXFP4 workload's input (bf16 4096x4096 N(0,1), 41 outlier channels x50), E4M3 scales "
+        "per 16, packed output + dequant with the inverse rotation",
+        (4096, 4096), 2, dict(outliers=41, outlier_gain=50.0)),
     "dualscale_pack": Workload(
         "dualscale_pack",
         "dual-scale micro-grouped FP4 pack/unpack, two-level FWHT 16x8: bf16 8192x8192 "

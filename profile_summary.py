@@ -74,6 +74,15 @@ CASES = {
         title="MXFP4 dequantization with inverse Hadamard-32 to bf16, 4096x4096 (rotating buffers)",
         bench=["--workload", "mxfp4_h32", "--op", "dequant"], steps=100, timed=100, pmc=[SQ_PASS],
         kernels={"k_dequant": ("mxfp4_h32_dequant", ["quant.hip"] + DEVICE_HPP, 42467328, None)}),
+    "k_quant_nv_h16_4096x4096": dict(
+        title="Hadamard-16 NVFP4 quantization with a calibrated (static) tensor scale, bf16 4096x4096 with 41 "
+              "outlier channels x50 (rotating buffers)",
+        bench=["--workload", "nvfp4_h16", "--op", "quant"], steps=100, timed=100, pmc=[SQ_PASS],
+        kernels={"k_quant_nv": ("nvfp4_h16_quant", ["quant.hip"] + DEVICE_HPP, 42991620, None)}),
+    "k_dequant_nv_h16_bf16_4096x4096": dict(
+        title="NVFP4 dequantization with inverse Hadamard-16 to bf16, 4096x4096 (rotating buffers)",
+        bench=["--workload", "nvfp4_h16", "--op", "dequant"], steps=100, timed=100, pmc=[SQ_PASS],
+        kernels={"k_dequant": ("nvfp4_h16_dequant", ["quant.hip"] + DEVICE_HPP, 42991620, None)}),
     "k_pack_8192x8192": dict(
         title="dual-scale FP4 pack with the two-level FWHT, bf16 8192x8192 Student-t(4) (rotating buffers)",
         bench=["--workload", "dualscale_pack", "--op", "quant"], steps=50, timed=50, pmc=[SQ_PASS],

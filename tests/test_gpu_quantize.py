@@ -212,6 +212,31 @@ def test_nvfp4_rotated(h):
     P.assert_values_close(_np(y), want, h, what="dequantized + inverse H")
 
 
+def test_nvfp4_h16_static_scale_full_size():
+    """The NVFP4 H16 workload as timed: bf16 4096 x 4096 (41 outlier channels x50), tensor
+    scale calibrated by a dynamic pass and then given; every row, and the inverse-H16 bf16
+    dequantization of the GPU's own codes."""
+    _log("nvfp4 H16 4096x4096, calibrated tensor scale")
+    xt = W.mxfp4_h32_input()
+    xg = xt.to(DEV)
+    ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fp4.fp4_quantize(xg, "nvfp4", 16, tensor_scale=ts)
+    gst = _np(ts)[0]
+    dbg = torch.empty(xt.shape, dtype=torch.float32, device=DEV)
+    codes, scales, _ = fp4.fp4_quantize(xg, "nvfp4", 16, tensor_scale=ts, mode="given", dbg_rotated=dbg)
+    assert _np(ts)[0] == gst                                   # given: read, not rewritten
+    xv = _vals(xt)
+    ref = nvfp4.quantize(xv, hadamard=16, tensor_scale_value=gst)
+    P.assert_values_close(_np(dbg), ref["y"], 16, what="rotated values")
+    P.check_e4m3_scales(_np(scales), ref["scales"], ref["scale_arg"])
+    c2 = nvfp4.quantize(xv, hadamard=16, tensor_scale_value=gst, block_scales=_np(scales))
+    n = P.check_e2m1_codes(F.unpack_nibbles(_np(codes)), c2["codes"], c2["elem_arg"], c2["y"], 16)
+    _log(f"  boundary-tolerated code differences: {n}")
+    y = fp4.fp4_dequantize(codes, scales, ts, "nvfp4", 16, torch.bfloat16)
+    want = nvfp4.dequantize(_np(codes), _np(scales), gst, inverse_hadamard=16)
+    P.assert_bf16_close(_vals(y.cpu()), want, 16)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 @pytest.mark.parametrize("h", [0, 16, 32, 128])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])

@@ -59,7 +59,8 @@ def test_column_shard_line():
     assert d["config"]["N"] == 3584 and "shard" in d["config"]["workload"]
 
 
-MEMORY_WORKLOADS = [("mxfp4_h32", "quant"), ("mxfp4_h32", "dequant"), ("dualscale_pack", "quant"),
+MEMORY_WORKLOADS = [("mxfp4_h32", "quant"), ("mxfp4_h32", "dequant"), ("nvfp4_h16", "quant"),
+                    ("nvfp4_h16", "dequant"), ("dualscale_pack", "quant"),
                     ("dualscale_pack", "dequant"), ("arcquant", "quant"), ("arcquant_gamma", "quant"),
                     ("arcquant_mx", "quant"), ("nvfp4_roundtrip", "quant")]
 
