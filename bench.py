@@ -311,7 +311,8 @@ def run_w4a4_gemm(args, name="w4a4_gemm"):
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
-    gemm_ms, quant_ms = tg.mean_ms(), tq.mean_ms()
+    gemm_ms, quant_step_ms = tg.mean_ms(), tq.mean_ms()
+    quant_ms = _quant_alone_ms(a_sets, a_codes, a_scales)
     quant_bytes = M * K * 2 + M * K // 2 + M * K // 32          # bf16 in, codes + E8M0 out
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
@@ -332,11 +333,38 @@ def run_w4a4_gemm(args, name="w4a4_gemm"):
         "roofline_quantize": {"bound": "hbm", "achieved": quant_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": quant_gbs / HBM_PEAK_GBS, "traffic": _traffic("quant_mx_h32_a"),
                               "kernel": "k_quant_mx<bf16,32>", "kernel_ms": quant_ms,
-                              "bytes_per_launch": quant_bytes},
+                              "kernel_ms_in_step": quant_step_ms, "bytes_per_launch": quant_bytes,
+                              "timing": "the A quantization alone: back-to-back launches over the same rotating "
+                                        "activation batches in one HIP graph, median of five replays "
+                                        "(kernel_ms_in_step: the event pair around it inside the timed steps, "
+                                        "which also holds its dispatch)"},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_gemm(a_cpu, w_cpu, rows=M)
     return out
+
+
+def _quant_alone_ms(a_sets, codes, scales, rounds=4, reps=5):
+    """Mean time per launch of the step's A quantization on its own: `rounds` passes over
+    the rotating activation batches captured into one HIP graph, five replays timed with
+    one event pair each on the replay stream; the median replay."""
+    g = torch.cuda.CUDAGraph()
+    n = rounds * len(a_sets)
+    with torch.cuda.graph(g):
+        for k in range(n):
+            fp4.fp4_quantize(a_sets[k % len(a_sets)], "mxfp4", 32, codes=codes, scales=scales)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
+    del g
+    return float(np.median(times))
 
 
 def run_w4a4_fused(args):

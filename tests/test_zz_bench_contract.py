@@ -38,6 +38,9 @@ def test_default_run_prints_the_contract_line():
     r = d["roofline"]
     assert r["bound"] in ("hbm", "mfma", "alu") and r["achieved"] > 0 and r["peak"] > 0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
+    q = d["roofline_quantize"]
+    assert q["bound"] == "hbm" and q["kernel_ms"] > 0 and q["kernel_ms_in_step"] > 0
+    assert abs(q["achieved"] - q["bytes_per_launch"] / (q["kernel_ms"] * 1e-3) / 1e9) < 1e-6 * q["achieved"]
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
 
